@@ -1,0 +1,110 @@
+"""Seeded synthetic inputs for the MoE block: shapes and random draws only.
+
+This module holds none of the method's arithmetic.  It is the one piece of code
+that both the HIP path's tests and the CPU oracle's tests use: it names the
+workload shapes and draws the tensors; nothing here scores, selects, sorts,
+multiplies or combines.
+
+Shapes follow the Beam MoE block ("Welcome Beam: a 501B open model you can own,
+customize, and scale", section "Mixture of Experts": hidden 5120, 256 experts
+in 8 groups of 32, 4 groups kept, 8 experts per token, intermediate 2560,
+output scale 2.5).  Trained weights are not available, so seeded Gaussians
+stand in for them: activations ~ N(0, 1), router and expert weights
+~ N(0, 0.02), all cast to bf16 with round-to-nearest-even.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, replace
+
+import torch
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    T: int
+    H: int
+    I: int
+    E: int
+    G: int
+    TG: int
+    k: int
+    scale: float
+    hot_groups: int = 0      # skew: number of groups holding biased experts
+    hot_per_group: int = 0   # skew: biased experts per hot group
+    hot_bias: float = 0.0    # skew: logit bias on each hot expert
+
+    def with_(self, **kw) -> "MoEConfig":
+        return replace(self, **kw)
+
+    @property
+    def pairs(self) -> int:
+        return self.T * self.k
+
+
+_BEAM = dict(H=5120, I=2560, E=256, G=8, TG=4, k=8, scale=2.5)
+
+CONFIGS = {
+    # small case the oracle finishes in well under a second
+    "tiny": MoEConfig("tiny", T=64, H=256, I=128, E=16, G=4, TG=2, k=4, scale=1.0),
+    # decode batch: weight-streaming (HBM-bound) regime
+    "decode": MoEConfig("decode", T=128, **_BEAM),
+    # prefill chunk: ~256 rows per expert
+    "prefill": MoEConfig("prefill", T=8192, **_BEAM),
+    # skewed routing: +3.0 logit bias on 8 experts in each of 2 seeded groups
+    "skew": MoEConfig("skew", T=4096, hot_groups=2, hot_per_group=8, hot_bias=3.0, **_BEAM),
+    # long prefill processed as one call
+    "long": MoEConfig("long", T=65536, **_BEAM),
+}
+
+ACT_STD = 1.0
+W_STD = 0.02
+
+
+def _randn_bf16(shape, std, gen, device, chunk_rows=None):
+    """N(0, std^2) drawn in fp32 and rounded to bf16; big tensors are drawn in
+    chunks along dim 0 to bound the fp32 temporary."""
+    out = torch.empty(shape, dtype=torch.bfloat16, device=device)
+    n0 = shape[0]
+    step = n0 if chunk_rows is None else max(1, chunk_rows)
+    for a in range(0, n0, step):
+        b = min(n0, a + step)
+        t = torch.randn((b - a, *shape[1:]), generator=gen, device=device, dtype=torch.float32)
+        if std != 1.0:
+            t.mul_(std)
+        out[a:b].copy_(t)
+        del t
+    return out
+
+
+def make_inputs(cfg: MoEConfig, seed: int = 0, device="cpu"):
+    """Draw x, router weight, router bias and the three expert weight stacks.
+
+    Draw order is fixed: x, w_router, hot-expert choice, w_gate, w_up, w_down.
+    Returns a dict of tensors on ``device``: x [T,H], w_router [E,H],
+    w_gate [E,I,H], w_up [E,I,H], w_down [E,H,I] (bf16) and bias [E] (fp32).
+    """
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    T, H, I, E, G = cfg.T, cfg.H, cfg.I, cfg.E, cfg.G
+    x = _randn_bf16((T, H), ACT_STD, gen, device, chunk_rows=8192)
+    w_router = _randn_bf16((E, H), W_STD, gen, device)
+    bias = torch.zeros(E, dtype=torch.float32, device=device)
+    if cfg.hot_groups > 0:
+        gsize = E // G
+        groups = torch.randperm(G, generator=gen, device=device)[: cfg.hot_groups]
+        for g in groups.tolist():
+            members = torch.randperm(gsize, generator=gen, device=device)[: cfg.hot_per_group]
+            bias[g * gsize + members] = cfg.hot_bias
+    per = 8 if E >= 64 else E
+    w_gate = _randn_bf16((E, I, H), W_STD, gen, device, chunk_rows=per)
+    w_up = _randn_bf16((E, I, H), W_STD, gen, device, chunk_rows=per)
+    w_down = _randn_bf16((E, H, I), W_STD, gen, device, chunk_rows=per)
+    return dict(x=x, w_router=w_router, bias=bias, w_gate=w_gate, w_up=w_up, w_down=w_down)
+
+
+def bits(t: torch.Tensor):
+    """bf16 tensor -> numpy uint16 bit patterns (host copy)."""
+    import numpy as np
+    return t.detach().contiguous().cpu().view(torch.int16).numpy().view(np.uint16)
