@@ -1,0 +1,37 @@
+// kernels.h -- internal launchers behind the C ABI (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+struct Problem {
+    int64_t T;
+    int H, I, E, G, TG, k;
+    float scale;
+};
+
+// Pairs handled by one block of the counting sort.
+constexpr int kPermuteChunk = 4096;
+
+inline int64_t permute_blocks(int64_t pairs) {
+    return pairs <= 0 ? 1 : (pairs + kPermuteChunk - 1) / kPermuteChunk;
+}
+
+hipError_t launch_route(const Problem& p, const uint16_t* x, const uint16_t* w_router,
+                        const float* bias, int32_t* ids, float* weights, hipStream_t s);
+
+hipError_t launch_permute(const Problem& p, const int32_t* ids, int32_t* offsets,
+                          int32_t* sorted_pairs, int32_t* pair_rows, int32_t* block_counts,
+                          hipStream_t s);
+
+hipError_t launch_expert_ffn(const Problem& p, const uint16_t* x, const int32_t* sorted_pairs,
+                             const int32_t* offsets, const uint16_t* w_gate,
+                             const uint16_t* w_up, const uint16_t* w_down, uint16_t* h, float* y,
+                             hipStream_t s);
+
+hipError_t launch_combine(const Problem& p, const float* y, const int32_t* pair_rows,
+                          const float* weights, void* out, bool out_bf16, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,251 @@
+// moe_api.hip -- the C ABI of libmoe.so (declared in include/moe.h).
+//
+// Host side only: argument checks, workspace layout and kernel launches.  All
+// checks run before the first HIP call, so a rejected call enqueues nothing
+// and touches no output.  No allocation, no synchronisation.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <string>
+
+#include "../../include/moe.h"
+#include "kernels.h"
+
+#define MOE_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+moe_status ok() {
+    g_last_error.clear();
+    return MOE_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+    size_t ids, weights, offsets, sorted, rows, counts, h, total;
+};
+
+Layout layout_of(const moe_problem& p) {
+    const size_t P = static_cast<size_t>(p.T) * static_cast<size_t>(p.k);
+    const size_t nb = static_cast<size_t>(moe::permute_blocks(static_cast<int64_t>(P)));
+    Layout L{};
+    size_t o = 0;
+    L.ids = o;     o += align_up(P * 4);
+    L.weights = o; o += align_up(P * 4);
+    L.offsets = o; o += align_up((static_cast<size_t>(p.E) + 1) * 4);
+    L.sorted = o;  o += align_up(P * 4);
+    L.rows = o;    o += align_up(P * 4);
+    L.counts = o;  o += align_up(nb * static_cast<size_t>(p.E) * 4);
+    L.h = o;       o += align_up(P * static_cast<size_t>(p.I) * 2);
+    L.total = o;
+    return L;
+}
+
+// Shape checks shared by every entry point.
+moe_status check_problem(const moe_problem* p) {
+    if (!p) return fail(MOE_ERR_INVALID_ARG, "problem is NULL");
+    if (p->T < 0) return fail(MOE_ERR_INVALID_ARG, "T=%lld < 0", (long long)p->T);
+    if (p->H <= 0 || p->H % 64 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "H=%d must be a positive multiple of 64", p->H);
+    if (p->I <= 0 || p->I % 64 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "I=%d must be a positive multiple of 64", p->I);
+    if (p->E <= 0) return fail(MOE_ERR_INVALID_ARG, "E=%d must be positive", p->E);
+    if (p->G <= 0 || p->E % p->G != 0)
+        return fail(MOE_ERR_INVALID_ARG, "G=%d must divide E=%d", p->G, p->E);
+    if (p->TG < 1 || p->TG > p->G)
+        return fail(MOE_ERR_INVALID_ARG, "TG=%d must be in [1, G=%d]", p->TG, p->G);
+    const int64_t cand = static_cast<int64_t>(p->TG) * (p->E / p->G);
+    if (p->k < 1 || p->k > cand)
+        return fail(MOE_ERR_INVALID_ARG, "k=%d must be in [1, TG*E/G=%lld]", p->k, (long long)cand);
+    if (!isfinite(p->scale)) return fail(MOE_ERR_INVALID_ARG, "scale is not finite");
+    if (p->T * static_cast<int64_t>(p->k) > 0x7fffffffLL)
+        return fail(MOE_ERR_INVALID_ARG, "T*k=%lld exceeds int32", (long long)(p->T * p->k));
+    if (p->E > 256) return fail(MOE_ERR_UNSUPPORTED, "E=%d > 256", p->E);
+    if (p->k > 16) return fail(MOE_ERR_UNSUPPORTED, "k=%d > 16", p->k);
+    if (p->H % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "H=%d is not a multiple of 128", p->H);
+    return MOE_OK;
+}
+
+moe_status check_ptr(const void* ptr, const char* name, bool nullable = false) {
+    if (!ptr) {
+        if (nullable) return MOE_OK;
+        return fail(MOE_ERR_INVALID_ARG, "%s is NULL", name);
+    }
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+        return fail(MOE_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+    return MOE_OK;
+}
+
+moe_status check_ws(const moe_problem& p, const void* ws, size_t ws_bytes) {
+    const size_t need = layout_of(p).total;
+    if (!ws) return fail(MOE_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", need);
+    if (reinterpret_cast<uintptr_t>(ws) % 16 != 0)
+        return fail(MOE_ERR_WORKSPACE, "workspace is not 16-byte aligned");
+    if (ws_bytes < need)
+        return fail(MOE_ERR_WORKSPACE, "workspace has %zu bytes, need %zu", ws_bytes, need);
+    return MOE_OK;
+}
+
+moe::Problem to_internal(const moe_problem& p) {
+    return moe::Problem{p.T, p.H, p.I, p.E, p.G, p.TG, p.k, p.scale};
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+#define MOE_TRY(expr)                      \
+    do {                                   \
+        const moe_status _s = (expr);      \
+        if (_s != MOE_OK) return _s;       \
+    } while (0)
+
+template <typename T>
+T* at(void* ws, size_t off) {
+    return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+MOE_EXPORT size_t moe_workspace_bytes(const moe_problem* p) {
+    if (check_problem(p) != MOE_OK) return 0;
+    return layout_of(*p).total;
+}
+
+MOE_EXPORT moe_status moe_route(const moe_problem* p, const moe_bf16* x, const moe_bf16* w_router,
+                                const float* bias, int32_t* topk_ids, float* topk_weights,
+                                hipStream_t stream) {
+    MOE_TRY(check_problem(p));
+    if (p->T == 0) return ok();
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(w_router, "w_router"));
+    MOE_TRY(check_ptr(bias, "bias", true));
+    MOE_TRY(check_ptr(topk_ids, "topk_ids"));
+    MOE_TRY(check_ptr(topk_weights, "topk_weights"));
+    return hip_status(moe::launch_route(to_internal(*p), x, w_router, bias, topk_ids, topk_weights,
+                                        stream),
+                      "route launch");
+}
+
+MOE_EXPORT moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids,
+                                  int32_t* expert_offsets, int32_t* sorted_pairs,
+                                  int32_t* pair_rows, void* ws, size_t ws_bytes,
+                                  hipStream_t stream) {
+    MOE_TRY(check_problem(p));
+    if (p->T == 0) return ok();
+    MOE_TRY(check_ptr(topk_ids, "topk_ids"));
+    MOE_TRY(check_ptr(expert_offsets, "expert_offsets"));
+    MOE_TRY(check_ptr(sorted_pairs, "sorted_pairs"));
+    MOE_TRY(check_ptr(pair_rows, "pair_rows"));
+    MOE_TRY(check_ws(*p, ws, ws_bytes));
+    const Layout L = layout_of(*p);
+    return hip_status(moe::launch_permute(to_internal(*p), topk_ids, expert_offsets, sorted_pairs,
+                                          pair_rows, at<int32_t>(ws, L.counts), stream),
+                      "permute launch");
+}
+
+MOE_EXPORT moe_status moe_expert_ffn(const moe_problem* p, const moe_bf16* x,
+                                     const int32_t* sorted_pairs, const int32_t* expert_offsets,
+                                     const moe_bf16* w_gate, const moe_bf16* w_up,
+                                     const moe_bf16* w_down, float* y, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+    MOE_TRY(check_problem(p));
+    if (p->T == 0) return ok();
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(sorted_pairs, "sorted_pairs"));
+    MOE_TRY(check_ptr(expert_offsets, "expert_offsets"));
+    MOE_TRY(check_ptr(w_gate, "w_gate"));
+    MOE_TRY(check_ptr(w_up, "w_up"));
+    MOE_TRY(check_ptr(w_down, "w_down"));
+    MOE_TRY(check_ptr(y, "y"));
+    MOE_TRY(check_ws(*p, ws, ws_bytes));
+    const Layout L = layout_of(*p);
+    return hip_status(moe::launch_expert_ffn(to_internal(*p), x, sorted_pairs, expert_offsets,
+                                             w_gate, w_up, w_down, at<uint16_t>(ws, L.h), y,
+                                             stream),
+                      "expert ffn launch");
+}
+
+MOE_EXPORT moe_status moe_combine(const moe_problem* p, const float* y, const int32_t* pair_rows,
+                                  const float* topk_weights, void* out, moe_dtype out_dtype,
+                                  hipStream_t stream) {
+    MOE_TRY(check_problem(p));
+    if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16)
+        return fail(MOE_ERR_INVALID_ARG, "out_dtype=%d is not MOE_DTYPE_F32/BF16", (int)out_dtype);
+    if (p->T == 0) return ok();
+    MOE_TRY(check_ptr(y, "y"));
+    MOE_TRY(check_ptr(pair_rows, "pair_rows"));
+    MOE_TRY(check_ptr(topk_weights, "topk_weights"));
+    MOE_TRY(check_ptr(out, "out"));
+    return hip_status(moe::launch_combine(to_internal(*p), y, pair_rows, topk_weights, out,
+                                          out_dtype == MOE_DTYPE_BF16, stream),
+                      "combine launch");
+}
+
+MOE_EXPORT moe_status moe_forward(const moe_problem* p, const moe_bf16* x,
+                                  const moe_bf16* w_router, const float* bias,
+                                  const moe_bf16* w_gate, const moe_bf16* w_up,
+                                  const moe_bf16* w_down, void* out, moe_dtype out_dtype,
+                                  int32_t* topk_ids, float* topk_weights, float* y, void* ws,
+                                  size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_problem(p));
+    if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16)
+        return fail(MOE_ERR_INVALID_ARG, "out_dtype=%d is not MOE_DTYPE_F32/BF16", (int)out_dtype);
+    if (p->T == 0) return ok();
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(w_router, "w_router"));
+    MOE_TRY(check_ptr(bias, "bias", true));
+    MOE_TRY(check_ptr(w_gate, "w_gate"));
+    MOE_TRY(check_ptr(w_up, "w_up"));
+    MOE_TRY(check_ptr(w_down, "w_down"));
+    MOE_TRY(check_ptr(out, "out"));
+    MOE_TRY(check_ptr(topk_ids, "topk_ids", true));
+    MOE_TRY(check_ptr(topk_weights, "topk_weights", true));
+    MOE_TRY(check_ptr(y, "y"));
+    MOE_TRY(check_ws(*p, ws, ws_bytes));
+    const Layout L = layout_of(*p);
+    const moe::Problem q = to_internal(*p);
+    int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, L.ids);
+    float* wts = topk_weights ? topk_weights : at<float>(ws, L.weights);
+    int32_t* off = at<int32_t>(ws, L.offsets);
+    int32_t* sorted = at<int32_t>(ws, L.sorted);
+    int32_t* rows = at<int32_t>(ws, L.rows);
+    hipError_t e = moe::launch_route(q, x, w_router, bias, ids, wts, stream);
+    if (e != hipSuccess) return hip_status(e, "route launch");
+    e = moe::launch_permute(q, ids, off, sorted, rows, at<int32_t>(ws, L.counts), stream);
+    if (e != hipSuccess) return hip_status(e, "permute launch");
+    e = moe::launch_expert_ffn(q, x, sorted, off, w_gate, w_up, w_down, at<uint16_t>(ws, L.h), y,
+                               stream);
+    if (e != hipSuccess) return hip_status(e, "expert ffn launch");
+    e = moe::launch_combine(q, y, rows, wts, out, out_dtype == MOE_DTYPE_BF16, stream);
+    return hip_status(e, "combine launch");
+}
+
+MOE_EXPORT const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    }
+    return "MOE_ERR_UNKNOWN";
+}
+
+MOE_EXPORT const char* moe_last_error(void) { return g_last_error.c_str(); }

@@ -77,31 +77,51 @@ def _randn_bf16(shape, std, gen, device, chunk_rows=None):
     return out
 
 
-def make_inputs(cfg: MoEConfig, seed: int = 0, device="cpu"):
-    """Draw x, router weight, router bias and the three expert weight stacks.
+WEIGHT_SEED_OFFSET = 1_000_003
 
-    Draw order is fixed: x, w_router, hot-expert choice, w_gate, w_up, w_down.
-    Returns a dict of tensors on ``device``: x [T,H], w_router [E,H],
-    w_gate [E,I,H], w_up [E,I,H], w_down [E,H,I] (bf16) and bias [E] (fp32).
-    """
+
+def make_tokens(cfg: MoEConfig, seed: int = 0, device="cpu"):
+    """Draw the activations x [T,H] (bf16) and the router bias [E] (fp32).
+
+    The bias is zero except for the skewed workload: ``hot_per_group`` experts
+    in each of ``hot_groups`` seeded groups get ``hot_bias``.  Draw order: x,
+    then the hot-group choice, then the hot experts inside each group."""
     device = torch.device(device)
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
-    T, H, I, E, G = cfg.T, cfg.H, cfg.I, cfg.E, cfg.G
-    x = _randn_bf16((T, H), ACT_STD, gen, device, chunk_rows=8192)
-    w_router = _randn_bf16((E, H), W_STD, gen, device)
-    bias = torch.zeros(E, dtype=torch.float32, device=device)
+    x = _randn_bf16((cfg.T, cfg.H), ACT_STD, gen, device, chunk_rows=8192)
+    bias = torch.zeros(cfg.E, dtype=torch.float32, device=device)
     if cfg.hot_groups > 0:
-        gsize = E // G
-        groups = torch.randperm(G, generator=gen, device=device)[: cfg.hot_groups]
+        gsize = cfg.E // cfg.G
+        groups = torch.randperm(cfg.G, generator=gen, device=device)[: cfg.hot_groups]
         for g in groups.tolist():
             members = torch.randperm(gsize, generator=gen, device=device)[: cfg.hot_per_group]
             bias[g * gsize + members] = cfg.hot_bias
+    return dict(x=x, bias=bias)
+
+
+def make_weights(cfg: MoEConfig, seed: int = 0, device="cpu"):
+    """Draw the router weight [E,H] and the expert stacks w_gate, w_up
+    [E,I,H] and w_down [E,H,I] (bf16), in that order, from a generator seeded
+    with seed + WEIGHT_SEED_OFFSET."""
+    device = torch.device(device)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed + WEIGHT_SEED_OFFSET)
+    E, H, I = cfg.E, cfg.H, cfg.I
     per = 8 if E >= 64 else E
+    w_router = _randn_bf16((E, H), W_STD, gen, device)
     w_gate = _randn_bf16((E, I, H), W_STD, gen, device, chunk_rows=per)
     w_up = _randn_bf16((E, I, H), W_STD, gen, device, chunk_rows=per)
     w_down = _randn_bf16((E, H, I), W_STD, gen, device, chunk_rows=per)
-    return dict(x=x, w_router=w_router, bias=bias, w_gate=w_gate, w_up=w_up, w_down=w_down)
+    return dict(w_router=w_router, w_gate=w_gate, w_up=w_up, w_down=w_down)
+
+
+def make_inputs(cfg: MoEConfig, seed: int = 0, device="cpu"):
+    """Tokens and weights of one workload: x, bias, w_router, w_gate, w_up,
+    w_down (see make_tokens and make_weights)."""
+    d = make_tokens(cfg, seed, device)
+    d.update(make_weights(cfg, seed, device))
+    return d
 
 
 def bits(t: torch.Tensor):

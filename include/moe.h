@@ -1,0 +1,154 @@
+/*
+ * moe.h -- C ABI of libmoe.so: forward pass of one Beam-style
+ * Mixture-of-Experts block on an AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Welcome Beam: a 501B open model you can own, customize, and
+ * scale", section "Mixture of Experts"; the same text is in "Reflection
+ * Releases Beam: An Open 501B MoE Model with 1M Context", section "Mixture of
+ * Experts"): a router gives each of E experts a sigmoid score; the experts
+ * form G groups of E/G consecutive indices; each group is ranked by the sum of
+ * its two best scores and the TG best groups are kept; the k best experts of
+ * the kept groups run on the token; their scores, normalised to sum to one,
+ * weight the expert outputs, and the sum is multiplied by a scale (2.5 for
+ * Beam).  Each expert is a SwiGLU MLP with intermediate size I.  Section
+ * "Residual Stream" of the first page fixes the router and the SwiGLU product
+ * in FP32.  Beam: H=5120, E=256, G=8, TG=4, k=8, I=2560, scale=2.5.
+ *
+ * Conventions for every call:
+ *  - All tensor pointers are device memory owned by the caller, contiguous,
+ *    row-major and 16-byte aligned.  bf16 tensors are passed as moe_bf16 (the
+ *    raw 16-bit pattern).
+ *  - The library never allocates, frees or synchronises; each call only
+ *    enqueues kernels on `stream` (0 = the null stream).
+ *  - Every argument is checked on the host before anything is enqueued.  On
+ *    any error nothing is enqueued and no output is touched; the call returns
+ *    a moe_status and moe_last_error() gives a message (per host thread).
+ *    MOE_ERR_HIP means a launch was refused by the HIP runtime; kernels of the
+ *    same call that were enqueued before it may have run.
+ *  - Routing ties go to the lower index, for groups and for experts.  Scores
+ *    are fp32; expert GEMMs multiply bf16 values and accumulate in fp32; the
+ *    SwiGLU product is rounded to bf16 (nearest-even) before the down
+ *    projection; expert outputs y stay fp32.
+ *  - No call uses atomics on its outputs: results are deterministic run to
+ *    run.
+ *  - Calls that share a workspace or outputs on one stream are ordered by the
+ *    stream; calls on different streams that share them race.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t moe_bf16; /* bf16 bit pattern */
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* null pointer, misalignment, inconsistent shape */
+    MOE_ERR_UNSUPPORTED = 2, /* valid problem outside the kernels' limits       */
+    MOE_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required      */
+    MOE_ERR_HIP = 4          /* the HIP runtime refused a launch                */
+} moe_status;
+
+typedef enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
+
+/* Problem shape.
+ *   T  tokens (>= 0; T = 0 is a no-op that returns MOE_OK)
+ *   H  hidden size,        H % 64 == 0 (H % 128 == 0 for the kernels)
+ *   I  expert intermediate size, I % 64 == 0
+ *   E  experts, 1 <= E <= 256
+ *   G  groups, E % G == 0; group g holds experts [g*E/G, (g+1)*E/G)
+ *   TG kept groups, 1 <= TG <= G
+ *   k  experts per token, 1 <= k <= TG*E/G and k <= 16
+ *   scale  factor applied to the weighted sum (2.5 for Beam)
+ * T*k must fit in int32. */
+typedef struct moe_problem {
+    int64_t T;
+    int32_t H, I, E, G, TG, k;
+    float scale;
+} moe_problem;
+
+/* Bytes of scratch every call below needs in `ws` for problem p (0 if p is
+ * invalid).  The largest part is the bf16 SwiGLU product [T*k, I].  One
+ * workspace sized by this function serves every call. */
+size_t moe_workspace_bytes(const moe_problem* p);
+
+/* Router and group-limited selection for T tokens.
+ *   x            [T,H] bf16 activations
+ *   w_router     [E,H] bf16 router weight
+ *   bias         [E] fp32 added to each logit before the sigmoid, or NULL (0)
+ *   topk_ids     [T,k] int32 out: chosen experts, best score first
+ *   topk_weights [T,k] fp32 out: chosen scores / their sum (sum to 1)
+ * Scores are sigmoid(x . w_router[e] + bias[e]) with fp32 accumulation. */
+moe_status moe_route(const moe_problem* p, const moe_bf16* x, const moe_bf16* w_router,
+                     const float* bias, int32_t* topk_ids, float* topk_weights,
+                     hipStream_t stream);
+
+/* Dispatch: stable counting sort of the T*k pairs p = t*k + j by expert.
+ *   topk_ids       [T,k] int32 in: expert of each pair, 0 <= id < E
+ *   expert_offsets [E+1] int32 out: first sorted position of each expert;
+ *                  expert_offsets[E] = T*k
+ *   sorted_pairs   [T*k] int32 out: pair ids grouped by expert, increasing
+ *                  pair id inside each expert
+ *   pair_rows      [T*k] int32 out: inverse of sorted_pairs
+ * Uses the permutation scratch of `ws`.  Ids outside [0,E) are dropped:
+ * their pair_rows entry is -1 and expert_offsets[E] counts only kept pairs. */
+moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, int32_t* expert_offsets,
+                       int32_t* sorted_pairs, int32_t* pair_rows, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Expert SwiGLU MLPs over the sorted pairs.
+ *   x              [T,H] bf16; row of pair q is x[sorted_pairs[q] / k]
+ *   sorted_pairs, expert_offsets   as written by moe_permute
+ *   w_gate, w_up   [E,I,H] bf16;  w_down [E,H,I] bf16
+ *   y              [T*k,H] fp32 out, sorted order: y[q] is the output of the
+ *                  expert that owns position q for the token of pair
+ *                  sorted_pairs[q]
+ * h[q] = bf16(silu(x_q . w_gate[e]^T) * (x_q . w_up[e]^T)) goes to `ws`;
+ * y[q] = h[q] . w_down[e]^T.  The tile schedule is derived on the device from
+ * expert_offsets, so no host read of device data is needed.  Rows of y past
+ * expert_offsets[E] are not written. */
+moe_status moe_expert_ffn(const moe_problem* p, const moe_bf16* x, const int32_t* sorted_pairs,
+                          const int32_t* expert_offsets, const moe_bf16* w_gate,
+                          const moe_bf16* w_up, const moe_bf16* w_down, float* y, void* ws,
+                          size_t ws_bytes, hipStream_t stream);
+
+/* Weighted recombination without atomics.
+ *   y            [T*k,H] fp32 in sorted order
+ *   pair_rows    [T*k] int32 (from moe_permute); -1 entries contribute 0
+ *   topk_weights [T,k] fp32
+ *   out          [T,H] fp32 or bf16 (out_dtype):
+ *                out[t] = scale * sum_{j=0..k-1} w[t,j] * y[pair_rows[t*k+j]],
+ *                summed in j order in fp32; bf16 output is the
+ *                round-to-nearest-even cast of that fp32 value. */
+moe_status moe_combine(const moe_problem* p, const float* y, const int32_t* pair_rows,
+                       const float* topk_weights, void* out, moe_dtype out_dtype,
+                       hipStream_t stream);
+
+/* The whole block: route, permute, expert FFN, combine.
+ *   topk_ids, topk_weights  optional [T,k] outputs (NULL: kept in `ws`)
+ *   y                       [T*k,H] fp32 caller buffer for expert outputs
+ *   out                     [T,H] in out_dtype */
+moe_status moe_forward(const moe_problem* p, const moe_bf16* x, const moe_bf16* w_router,
+                       const float* bias, const moe_bf16* w_gate, const moe_bf16* w_up,
+                       const moe_bf16* w_down, void* out, moe_dtype out_dtype, int32_t* topk_ids,
+                       float* topk_weights, float* y, void* ws, size_t ws_bytes,
+                       hipStream_t stream);
+
+/* Static text for a status code. */
+const char* moe_status_string(moe_status s);
+
+/* Message of the last failed call on this host thread ("" if none). */
+const char* moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

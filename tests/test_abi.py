@@ -1,0 +1,129 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/moe.h declares, sizes workspaces, and rejects bad arguments on the
+host before any HIP call (nothing enqueued, outputs untouched)."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import torch  # noqa: F401  (the binding binds to torch's HIP runtime)
+    from group_limited_routing_router_amd import moe
+    return moe
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function(lib):
+    names = _declared()
+    assert set(names) == set(lib.EXPORTS)
+    cdll = lib.load_library()
+    for n in names:
+        assert hasattr(cdll, n), n
+
+
+def test_single_hip_runtime(lib):
+    lib.load_library()
+    assert len(lib._hip_runtimes_mapped()) <= 1
+
+
+def _beam(T=128):
+    from group_limited_routing_router_amd.moe import MoEProblem
+    return MoEProblem(T, 5120, 2560, 256, 8, 4, 8, 2.5)
+
+
+def test_workspace_bytes(lib):
+    for T in (1, 128, 8192, 65536):
+        p = _beam(T)
+        n = lib.moe_workspace_bytes(p)
+        assert n >= T * 8 * 2560 * 2          # bf16 SwiGLU product
+        assert n < T * 8 * 2560 * 2 + T * 8 * 64 + (1 << 22)
+    assert lib.moe_workspace_bytes(_beam(0)) >= 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("T", -1, 1), ("H", 100, 1), ("H", 0, 1), ("I", 96, 1), ("E", 0, 1), ("G", 7, 1),
+    ("TG", 0, 1), ("TG", 9, 1), ("k", 0, 1), ("k", 129, 1), ("E", 512, 1), ("k", 17, 2),
+    ("H", 192, 2),
+])
+def test_problem_validation(lib, field, value, status):
+    p = _beam()
+    setattr(p, field, value)
+    if field == "E" and value == 512:
+        p.G = 8  # divisible, valid shape but beyond the kernels' limit
+        status = 2
+    cdll = lib.load_library()
+    buf = np.zeros(64, np.int32)
+    out = np.full(64, 7, np.float32)
+    ptr = buf.ctypes.data
+    rc = cdll.moe_route(ctypes.byref(p), ptr, ptr, None, ptr, out.ctypes.data, None)
+    assert rc == status, cdll.moe_last_error()
+    assert cdll.moe_last_error()
+    assert np.all(out == 7)
+    assert lib.moe_workspace_bytes(p) == 0
+
+
+def _aligned(n=4096, offset=0):
+    raw = np.zeros(n + 64, np.uint8)
+    base = (-raw.ctypes.data) % 64
+    return raw, raw.ctypes.data + base + offset
+
+
+def test_pointer_and_workspace_errors(lib):
+    cdll = lib.load_library()
+    p = _beam()
+    keep, good = _aligned()
+    keep2, odd = _aligned(offset=4)
+    guard = np.full(16, 3, np.int32)
+    # NULL inputs
+    assert cdll.moe_route(ctypes.byref(p), None, good, None, good, good, None) == 1
+    assert b"x" in cdll.moe_last_error()
+    # misaligned output
+    assert cdll.moe_route(ctypes.byref(p), good, good, None, odd, good, None) == 1
+    assert b"aligned" in cdll.moe_last_error()
+    # workspace too small / NULL
+    need = lib.moe_workspace_bytes(p)
+    assert cdll.moe_permute(ctypes.byref(p), good, good, good, good, good, need - 1, None) == 3
+    assert cdll.moe_permute(ctypes.byref(p), good, good, good, good, None, need, None) == 3
+    assert cdll.moe_expert_ffn(ctypes.byref(p), good, good, good, good, good, good, good, good,
+                               16, None) == 3
+    # bad output dtype
+    assert cdll.moe_combine(ctypes.byref(p), good, good, good, good, 5, None) == 1
+    assert cdll.moe_forward(ctypes.byref(p), good, good, None, good, good, good,
+                            guard.ctypes.data, 9, None, None, good, good, need, None) == 1
+    # forward: y missing
+    assert cdll.moe_forward(ctypes.byref(p), good, good, None, good, good, good,
+                            guard.ctypes.data, 0, None, None, None, good, need, None) == 1
+    assert np.all(guard == 3)
+    assert cdll.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
+
+
+def test_zero_tokens_is_a_noop(lib):
+    cdll = lib.load_library()
+    p = _beam(0)
+    assert cdll.moe_route(ctypes.byref(p), None, None, None, None, None, None) == 0
+    assert cdll.moe_permute(ctypes.byref(p), None, None, None, None, None, 0, None) == 0
+    assert cdll.moe_expert_ffn(ctypes.byref(p), None, None, None, None, None, None, None, None,
+                               0, None) == 0
+    assert cdll.moe_combine(ctypes.byref(p), None, None, None, None, 0, None) == 0
+    assert cdll.moe_forward(ctypes.byref(p), None, None, None, None, None, None, None, 0, None,
+                            None, None, None, 0, None) == 0
+
+
+def test_binding_raises_with_message(lib):
+    p = _beam()
+    p.G = 3
+    with pytest.raises(lib.MoEError) as ei:
+        lib.moe_route(p, 0, 0, None, 0, 0, stream=0)
+    assert "G=3" in str(ei.value)

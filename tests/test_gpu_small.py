@@ -1,0 +1,176 @@
+"""GPU parity on small shapes: every C-ABI call against the oracle, element by
+element, on seeded inputs that span several tiles and ragged tails, plus the
+degenerate cases of the method (k=1, k=E with one group, groups of one
+expert, every token on the same experts, exact ties)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from group_limited_routing_router_amd.inputs import CONFIGS, MoEConfig, bits, make_inputs
+
+from _parity import OUT_TOL, compare_routing, out_error
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from group_limited_routing_router_amd import moe as m
+    m.load_library()
+    return m
+
+
+def _to_gpu(d):
+    return {k: v.cuda() for k, v in d.items()}
+
+
+def _run_steps(moe, cfg, g, bias=True):
+    p = moe.MoEProblem.from_config(cfg)
+    b = moe.alloc_buffers(p)
+    moe.moe_route(p, g["x"], g["w_router"], g["bias"] if bias else None, b["topk_ids"],
+                  b["topk_weights"])
+    moe.moe_permute(p, b["topk_ids"], b["expert_offsets"], b["sorted_pairs"], b["pair_rows"],
+                    b["ws"])
+    moe.moe_expert_ffn(p, g["x"], b["sorted_pairs"], b["expert_offsets"], g["w_gate"], g["w_up"],
+                       g["w_down"], b["y"], b["ws"])
+    moe.moe_combine(p, b["y"], b["pair_rows"], b["topk_weights"], b["out"])
+    torch.cuda.synchronize()
+    return p, {k: v.cpu().numpy() if v.dtype != torch.bfloat16 else v.cpu() for k, v in b.items()}
+
+
+def _check_all(moe, cfg, d, label):
+    print(f"[case] {label} T={cfg.T} H={cfg.H} I={cfg.I} E={cfg.E} G={cfg.G} TG={cfg.TG} "
+          f"k={cfg.k}", flush=True)
+    g = _to_gpu(d)
+    p, r = _run_steps(moe, cfg, g)
+    xb, wrb = bits(d["x"]), bits(d["w_router"])
+    wgb, wub, wdb = bits(d["w_gate"]), bits(d["w_up"]), bits(d["w_down"])
+    bias = d["bias"].numpy()
+    # 1. routing
+    o_ids, o_w, s, gs = oracle.route(xb, wrb, bias, cfg.G, cfg.TG, cfg.k, want_scores=True)
+    exempt, st = compare_routing(r["topk_ids"], r["topk_weights"], o_ids, o_w, s, gs,
+                                 cfg.E, cfg.G, cfg.TG, cfg.k)
+    # 2. permutation of the GPU's own ids: bit-exact
+    off, sp, pr = oracle.permute(r["topk_ids"], cfg.E)
+    np.testing.assert_array_equal(r["expert_offsets"], off)
+    np.testing.assert_array_equal(r["sorted_pairs"], sp)
+    np.testing.assert_array_equal(r["pair_rows"], pr)
+    # 3. expert FFN on the GPU's routing: y in sorted order
+    ids_flat = r["topk_ids"].ravel()
+    tok = (sp // cfg.k).astype(np.int32)
+    exp = ids_flat[sp].astype(np.int32)
+    y_ref, _ = oracle.ffn_pairs(tok, exp, xb, wgb, wub, wdb)
+    ey, _ = out_error(r["y"], y_ref)
+    assert ey <= OUT_TOL, f"y err {ey}"
+    # 4. combine of the GPU's y: tight, only fp32 rounding differs
+    y_pairs = r["y"][pr]
+    out_c = oracle.combine(y_pairs, r["topk_weights"], cfg.scale)
+    ec, _ = out_error(r["out"], out_c)
+    assert ec <= 1e-5, f"combine err {ec}"
+    # 5. end to end against the oracle's own routing (GPU routing on exempt tokens)
+    ref = oracle.forward(xb, wrb, bias, wgb, wub, wdb, cfg.G, cfg.TG, cfg.k, cfg.scale)["out"]
+    if exempt.any():
+        inj, _, _ = oracle.forward_with_routing(xb, r["topk_ids"], r["topk_weights"], wgb, wub,
+                                                wdb, cfg.scale)
+        ref[exempt] = inj[exempt]
+    eo, rms = out_error(r["out"], ref)
+    print(f"    exempt={st['exempt']} y_err/rms={ey:.2e} out_err/rms={eo:.2e}", flush=True)
+    assert eo <= OUT_TOL
+    return g, r
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny_all_steps(moe, seed):
+    cfg = CONFIGS["tiny"]
+    _check_all(moe, cfg, make_inputs(cfg, seed=seed), f"tiny seed={seed}")
+
+
+SHAPES = [
+    # (T, H, I, E, G, TG, k) -- chosen to hit every tile configuration,
+    # ragged row tails and partial token tiles of the router
+    (1, 256, 128, 16, 4, 2, 4),
+    (17, 384, 192, 32, 4, 2, 6),
+    (200, 256, 64, 64, 8, 3, 8),
+    (300, 512, 256, 256, 8, 4, 8),
+    (1000, 256, 128, 32, 4, 2, 2),
+    (3000, 256, 128, 16, 4, 2, 4),
+    (5000, 128, 64, 16, 4, 2, 4),
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=lambda s: "T%d_H%d_I%d_E%d_G%d_TG%d_k%d" % s)
+def test_shapes(moe, shape):
+    T, H, I, E, G, TG, k = shape
+    cfg = MoEConfig("sweep", T=T, H=H, I=I, E=E, G=G, TG=TG, k=k, scale=2.5)
+    _check_all(moe, cfg, make_inputs(cfg, seed=T), "sweep")
+
+
+def test_dense_all_experts(moe):
+    """k = E with one group: the dense mixture over all experts."""
+    cfg = MoEConfig("dense", T=96, H=256, I=128, E=16, G=1, TG=1, k=16, scale=1.0)
+    _check_all(moe, cfg, make_inputs(cfg, seed=5), "dense k=E")
+
+
+def test_k1_and_groups_of_one(moe):
+    cfg = MoEConfig("k1", T=130, H=128, I=64, E=8, G=8, TG=8, k=1, scale=2.5)
+    _check_all(moe, cfg, make_inputs(cfg, seed=6), "k=1, group size 1")
+    cfg = MoEConfig("g1", T=70, H=256, I=128, E=32, G=32, TG=5, k=3, scale=2.5)
+    _check_all(moe, cfg, make_inputs(cfg, seed=7), "groups of one expert")
+
+
+def test_all_tokens_on_same_experts(moe):
+    """Extreme skew: a +6 logit bias on 4 experts sends every token there."""
+    cfg = MoEConfig("skewed", T=700, H=256, I=128, E=32, G=4, TG=2, k=4, scale=2.5)
+    d = make_inputs(cfg, seed=8)
+    d["bias"][[5, 6, 9, 12]] = 6.0
+    g, r = _check_all(moe, cfg, d, "all tokens on 4 experts")
+    counts = np.diff(r["expert_offsets"])
+    assert counts[[5, 6, 9, 12]].sum() >= 0.95 * cfg.T * cfg.k
+
+
+def test_exact_ties_lower_index(moe):
+    """Duplicate router rows give identical logits on any summation order; a
+    +100 bias saturates the sigmoid to 1.0.  The lower index must win."""
+    cfg = CONFIGS["tiny"]
+    d = make_inputs(cfg, seed=4)
+    d["w_router"][9] = d["w_router"][3]
+    d["w_router"][2] = d["w_router"][3]
+    d["bias"][[1, 3]] = 100.0
+    g, r = _check_all(moe, cfg, d, "ties")
+    assert np.all(r["topk_ids"][:, 0] == 1) and np.all(r["topk_ids"][:, 1] == 3)
+
+
+def test_forward_matches_steps_bf16_and_determinism(moe):
+    cfg = CONFIGS["tiny"].with_(T=333, scale=2.5)
+    d = make_inputs(cfg, seed=9)
+    g = _to_gpu(d)
+    p, r = _run_steps(moe, cfg, g)
+    outs = []
+    for dtype in (torch.float32, torch.float32, torch.bfloat16):
+        b = moe.alloc_buffers(p, out_dtype=dtype)
+        moe.moe_forward(p, g["x"], g["w_router"], g["bias"], g["w_gate"], g["w_up"], g["w_down"],
+                        b["out"], b["topk_ids"], b["topk_weights"], b["y"], b["ws"])
+        torch.cuda.synchronize()
+        outs.append(b["out"].cpu())
+        np.testing.assert_array_equal(b["topk_ids"].cpu().numpy(), r["topk_ids"])
+    # the composed call equals the four steps, bit for bit, and repeats exactly
+    np.testing.assert_array_equal(outs[0].numpy(), r["out"])
+    assert torch.equal(outs[0], outs[1])
+    # bf16 output is the round-to-nearest-even cast of the fp32 output
+    assert torch.equal(outs[2].view(torch.int16), outs[0].to(torch.bfloat16).view(torch.int16))
+    # forward without routing outputs (kept in the workspace) gives the same out
+    b = moe.alloc_buffers(p)
+    moe.moe_forward(p, g["x"], g["w_router"], g["bias"], g["w_gate"], g["w_up"], g["w_down"],
+                    b["out"], None, None, b["y"], b["ws"])
+    torch.cuda.synchronize()
+    assert torch.equal(b["out"].cpu(), outs[0])
+
+
+def test_zero_tokens_gpu(moe):
+    cfg = CONFIGS["tiny"]
+    p = moe.MoEProblem.from_config(cfg, T=0)
+    b = moe.alloc_buffers(p)
+    moe.moe_forward(p, None, None, None, None, None, None, b["out"], None, None, None, None)
+    torch.cuda.synchronize()
