@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of one Beam-shaped MoE block forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill]
+
+A step is one moe_forward call (router, group-limited top-k, permutation,
+gate/up + SwiGLU GEMM, down GEMM, weighted combine) over T tokens that are
+already resident in HBM.  The default workload is the prefill chunk: T=8192
+tokens, hidden 5120, 256 experts in 8 groups (4 kept), k=8, intermediate
+2560, bf16 weights and activations with fp32 accumulation; the decode batch
+(T=128) is timed as well because its HBM-bandwidth fraction is the other half
+of the headline metric.  Inputs are seeded synthetic Gaussians (no trained
+weights exist here).
+
+Prints one JSON line.  `value` is tokens/s of the timed workload; `roofline`
+describes the dominant kernel (timed with HIP events on the stream the
+library launches on); `cpu_baseline` is the CPU oracle timed on a bounded
+sample of the same workload on this host's cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5166e15   # dense bf16 MFMA, FLOP/s (MI355X published)
+PEAK_HBM = 8.0e12       # HBM3E, B/s (MI355X published)
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["group_limited_routing_router_amd/csrc/ffn.hip",
+                  "group_limited_routing_router_amd/csrc/common.h"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def work_counts(cfg, n_hit):
+    """Algorithmic FLOPs and HBM bytes of each step (what the method must do:
+    no padding, no intermediate round trips) -- see the design doc."""
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    P = T * k
+    w_expert = 3 * I * H * 2  # bytes of one expert's three bf16 matrices
+    c = {
+        "route": dict(flops=2 * T * H * E, bytes=T * H * 2 + E * H * 2 + P * 8),
+        "permute": dict(flops=0, bytes=P * 4 + (E + 1) * 4 + 2 * P * 4),
+        "gate_up": dict(flops=4 * P * H * I, bytes=n_hit * 2 * I * H * 2 + T * H * 2 + P * I * 2),
+        "down": dict(flops=2 * P * I * H, bytes=n_hit * I * H * 2 + P * I * 2 + P * H * 4),
+        "combine": dict(flops=2 * P * H, bytes=P * H * 4 + P * 8 + T * H * 4),
+    }
+    layer = dict(flops=2 * T * H * E + 6 * P * H * I,
+                 bytes=n_hit * w_expert + E * H * 2 + T * H * 2 + T * H * 4)
+    return c, layer
+
+
+def run_workload(name, steps, warmup, weights, want_kernels=True):
+    import torch
+
+    from group_limited_routing_router_amd import moe
+    from group_limited_routing_router_amd.inputs import CONFIGS, make_tokens
+
+    cfg = CONFIGS[name]
+    d = make_tokens(cfg, seed=0, device="cuda")
+    d.update(weights)
+    p = moe.MoEProblem.from_config(cfg)
+    b = moe.alloc_buffers(p)
+
+    def step():
+        moe.moe_forward(p, d["x"], d["w_router"], d["bias"], d["w_gate"], d["w_up"], d["w_down"],
+                        b["out"], b["topk_ids"], b["topk_weights"], b["y"], b["ws"])
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = wall * 1e3 / steps
+
+    ids = b["topk_ids"]
+    n_hit = int((torch.bincount(ids.flatten().long(), minlength=cfg.E) > 0).sum())
+    counts, layer = work_counts(cfg, n_hit)
+    res = dict(cfg=cfg, ms=ms, n_hit=n_hit, counts=counts, layer=layer, buffers=b, inputs=d)
+
+    if want_kernels:
+        # the same steps as separate calls, each bracketed by events on the
+        # current stream (the stream the library launches on)
+        names = ["route", "permute", "gate_up", "down", "combine"]
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+              for _ in range(steps)]
+        for it in range(warmup + steps):
+            e = ev[it - warmup] if it >= warmup else None
+            if e: e[0].record()
+            moe.moe_route(p, d["x"], d["w_router"], d["bias"], b["topk_ids"], b["topk_weights"])
+            if e: e[1].record()
+            moe.moe_permute(p, b["topk_ids"], b["expert_offsets"], b["sorted_pairs"],
+                            b["pair_rows"], b["ws"])
+            if e: e[2].record()
+            moe.moe_expert_gate_up(p, d["x"], b["sorted_pairs"], b["expert_offsets"],
+                                   d["w_gate"], d["w_up"], b["h"])
+            if e: e[3].record()
+            moe.moe_expert_down(p, b["h"], b["expert_offsets"], d["w_down"], b["y"])
+            if e: e[4].record()
+            moe.moe_combine(p, b["y"], b["pair_rows"], b["topk_weights"], b["out"])
+            if e: e[5].record()
+        torch.cuda.synchronize()
+        kt = {}
+        for j, nm in enumerate(names):
+            kt[nm] = sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps
+        res["kernel_ms"] = kt
+    return res
+
+
+def roofline_for(res, kernel):
+    c = res["counts"][kernel]
+    ms = res["kernel_ms"][kernel]
+    t_mfma = c["flops"] / PEAK_BF16
+    t_hbm = c["bytes"] / PEAK_HBM
+    traffic = None
+    try:
+        with open(TRAFFIC_FILE) as f:
+            tr = json.load(f)
+        ent = tr.get(res["cfg"].name, {}).get(kernel)
+        if ent and tr.get("kernel_source_sha") == kernel_source_sha():
+            traffic = int(ent["fetch_bytes"] + ent["write_bytes"])
+    except (OSError, ValueError, KeyError):
+        traffic = None
+    if t_hbm >= t_mfma:
+        ach = c["bytes"] / (ms * 1e-3) / 1e9
+        r = dict(bound="hbm", achieved=round(ach, 1), peak=PEAK_HBM / 1e9, unit="GB/s",
+                 frac=round(ach / (PEAK_HBM / 1e9), 4), traffic=traffic)
+    else:
+        ach = c["flops"] / (ms * 1e-3) / 1e12
+        r = dict(bound="mfma", achieved=round(ach, 1), peak=PEAK_BF16 / 1e12, unit="TFLOP/s",
+                 frac=round(ach / (PEAK_BF16 / 1e12), 4), traffic=traffic)
+    r["kernel"] = kernel
+    r["ms"] = round(ms, 4)
+    r["algorithmic_bytes"] = c["bytes"]
+    r["algorithmic_flops"] = c["flops"]
+    r["mfma_frac"] = round(c["flops"] / (ms * 1e-3) / PEAK_BF16, 4)
+    r["hbm_frac"] = round(c["bytes"] / (ms * 1e-3) / PEAK_HBM, 4)
+    return r
+
+
+def cpu_baseline(res, target_s):
+    """The oracle, as it stands, on a bounded sample of the timed workload's
+    tokens (routing + expert FFN + combine for the first n tokens)."""
+    import numpy as np
+    import torch
+
+    if "OMP_NUM_THREADS" not in os.environ:
+        os.environ["OMP_NUM_THREADS"] = str(len(os.sched_getaffinity(0)))
+    threads = int(os.environ["OMP_NUM_THREADS"])
+    import oracle
+    from group_limited_routing_router_amd.inputs import bits
+
+    cfg, d = res["cfg"], res["inputs"]
+    wr = bits(d["w_router"])
+    bias = d["bias"].cpu().numpy()
+
+    def run(n):
+        xs = bits(d["x"][:n])
+        t0 = time.perf_counter()
+        ids, w, _, _ = oracle.route(xs, wr, bias, cfg.G, cfg.TG, cfg.k)
+        t_route = time.perf_counter() - t0
+        used = np.unique(ids)
+        sel = torch.from_numpy(used).cuda()
+        wg = bits(d["w_gate"].index_select(0, sel))       # host copies: not timed
+        wu = bits(d["w_up"].index_select(0, sel))
+        wd = bits(d["w_down"].index_select(0, sel))
+        remap = np.full(cfg.E, -1, np.int32)
+        remap[used] = np.arange(len(used), dtype=np.int32)
+        t1 = time.perf_counter()
+        oracle.forward_with_routing(xs, remap[ids], w, wg, wu, wd, cfg.scale)
+        t_ffn = time.perf_counter() - t1
+        return t_route + t_ffn
+
+    n0 = 2
+    t0 = run(n0)
+    n = int(max(4, min(cfg.T, round(target_s / max(t0 / n0, 1e-6)))))
+    t = run(n)
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return dict(value=round(n / t, 2), unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"first {n} of the {cfg.T} tokens of the {cfg.name} workload: "
+                       f"routing, expert FFN and combine ({t:.1f} s)",
+                cpu_model=model)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "decode", "skew", "long"])
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the secondary decode (T=128) measurement")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from group_limited_routing_router_amd import moe
+    from group_limited_routing_router_amd.inputs import CONFIGS, make_weights
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.load_library()
+    weights = make_weights(CONFIGS["decode"], seed=0, device="cuda")
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        bb = torch.empty_like(a)
+        for _ in range(3):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+        del a, bb
+
+    main_res = run_workload(args.workload, args.steps, args.warmup, weights)
+    cfg = main_res["cfg"]
+    kms = main_res["kernel_ms"]
+    log("[bench] %s T=%d: %.3f ms/step; kernels %s" % (
+        cfg.name, cfg.T, main_res["ms"], {k: round(v, 4) for k, v in kms.items()}))
+    dominant = max(kms, key=kms.get)
+    layer = main_res["layer"]
+    ms = main_res["ms"]
+    out = {
+        "metric": "MoE-layer tokens/s + % bf16 MFMA peak (T=8192); % HBM peak BW (T=128)",
+        "value": round(cfg.T * args.steps / (ms * 1e-3 * args.steps), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"beam-moe-{cfg.name}", "tokens": cfg.T, "hidden": cfg.H,
+                   "intermediate": cfg.I, "experts": cfg.E, "groups": cfg.G,
+                   "kept_groups": cfg.TG, "top_k": cfg.k, "scale": cfg.scale,
+                   "experts_hit": main_res["n_hit"]},
+        "layer": {"tflops": round(layer["flops"] / (ms * 1e-3) / 1e12, 1),
+                  "mfma_frac": round(layer["flops"] / (ms * 1e-3) / PEAK_BF16, 4),
+                  "hbm_gbs": round(layer["bytes"] / (ms * 1e-3) / 1e9, 1),
+                  "hbm_frac": round(layer["bytes"] / (ms * 1e-3) / PEAK_HBM, 4)},
+        "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
+        "roofline": roofline_for(main_res, dominant),
+    }
+    if not args.no_decode and args.workload != "decode":
+        dec = run_workload("decode", args.steps, args.warmup, weights)
+        dl = dec["layer"]
+        out["decode"] = {
+            "tokens": dec["cfg"].T, "ms_per_step": round(dec["ms"], 4),
+            "tokens_per_s": round(dec["cfg"].T / (dec["ms"] * 1e-3), 1),
+            "experts_hit": dec["n_hit"],
+            "hbm_gbs": round(dl["bytes"] / (dec["ms"] * 1e-3) / 1e9, 1),
+            "hbm_frac": round(dl["bytes"] / (dec["ms"] * 1e-3) / PEAK_HBM, 4),
+            "kernels_ms": {k: round(v, 4) for k, v in dec["kernel_ms"].items()},
+        }
+        log("[bench] decode T=128: %.3f ms/step, %.1f%% of HBM peak" % (
+            dec["ms"], 100 * out["decode"]["hbm_frac"]))
+        del dec
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(main_res, args.cpu_seconds)
+        log("[bench] cpu oracle: %s" % out["cpu_baseline"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -8,6 +8,7 @@ namespace moe {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -35,6 +36,15 @@ __device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + ex
 // chunk (l / 16); it receives rows 4*(l/16) .. 4*(l/16)+3 of column (l % 16).
 __device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// One 32x32x16 bf16 MFMA step: acc += A(32x16) * B(16x32).  Lane l supplies
+// row (l % 32) of A and column (l % 32) of B, both for the 8 consecutive k of
+// half (l / 32); for i = 0..15 it receives row 8*(i/4) + 4*(l/32) + (i%4) of
+// column (l % 32).  Twice the work of the 16x16x32 form per issue: on gfx950
+// it is the shape that reaches the bf16 peak.
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4& v) {

@@ -27,6 +27,8 @@
 // then column tile, then row tile), so the tiles of one expert share its
 // gathered activations and, across row tiles, its weight tiles in that XCD's
 // L2.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -38,6 +40,13 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxE = 256;
 constexpr int BK = 64;           // K elements per LDS stage
 constexpr int LDS_STRIDE = BK + 8;  // bf16 per LDS row (16 B pad)
+
+// Raw buffer resource over [base, base + bytes): 32-bit offsets from one
+// scalar base; loads past `bytes` return zero.  Third dword: gfx9 default.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                             static_cast<int>(bytes), 0x00020000);
+}
 
 struct FfnArgs {
     int64_t P;       // pairs (rows of h and y)
@@ -53,6 +62,68 @@ struct FfnArgs {
     const uint16_t* b1;      // w_up [E,I,H] (gate/up only)
     void* out;               // h [P,I] bf16 (gate/up) or y [P,H] fp32 (down)
 };
+
+// Map this workgroup to a tile (expert e, column tile nt, row range
+// [row0, row0 + rows)).  Every workgroup rebuilds the prefix sum of per-expert
+// row tiles from expert_offsets in LDS (no host read-back); an expert with n
+// rows gets ceil(n / BM) row tiles of balanced size.  Workgroup b runs on XCD
+// b % 8; XCD x takes the x-th contiguous run of the tile list, ordered expert,
+// then column tile, then row tile, so the row tiles that share a weight tile
+// are neighbours on one XCD.  Returns false for surplus workgroups (uniform
+// over the workgroup).
+template <int BM>
+__device__ bool find_tile(const FfnArgs& a, int ncol_tiles, int32_t* s_off, int32_t* s_tstart,
+                          int& e_out, int& nt_out, int& row0_out, int& rows_out) {
+    const int tid = threadIdx.x;
+    const int E = a.E;
+    for (int e = tid; e <= E; e += kThreads) {
+        int64_t o = a.offsets[e];
+        o = o < 0 ? 0 : (o > a.P ? a.P : o);
+        s_off[e] = static_cast<int32_t>(o);
+    }
+    __syncthreads();
+    int cnt = 0;
+    if (tid < E) {
+        const int n = s_off[tid + 1] - s_off[tid];
+        cnt = n > 0 ? (n + BM - 1) / BM : 0;
+    }
+    s_tstart[tid] = cnt;  // kThreads == kMaxE
+    __syncthreads();
+    for (int d = 1; d < kThreads; d <<= 1) {
+        const int v = tid >= d ? s_tstart[tid - d] : 0;
+        __syncthreads();
+        s_tstart[tid] += v;
+        __syncthreads();
+    }
+    const int incl = s_tstart[tid];
+    __syncthreads();
+    s_tstart[tid + 1] = incl;  // exclusive prefix; s_tstart[E] = total row tiles
+    if (tid == 0) s_tstart[0] = 0;
+    __syncthreads();
+    const int64_t total = static_cast<int64_t>(s_tstart[E]) * ncol_tiles;
+    const int xcd = blockIdx.x % kNumXcd;
+    const int64_t local = blockIdx.x / kNumXcd;
+    const int64_t per = total / kNumXcd, rem = total % kNumXcd;
+    if (local >= per + (xcd < rem ? 1 : 0)) return false;
+    const int64_t L = xcd * per + (xcd < rem ? xcd : rem) + local;
+    int lo = 0, hi = E - 1;  // last e with s_tstart[e] * ncol_tiles <= L
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (static_cast<int64_t>(s_tstart[mid]) * ncol_tiles <= L) lo = mid; else hi = mid - 1;
+    }
+    const int e = lo;
+    const int tiles_e = s_tstart[e + 1] - s_tstart[e];  // >= 1 for the expert found
+    const int64_t rel = L - static_cast<int64_t>(s_tstart[e]) * ncol_tiles;
+    const int nt = static_cast<int>(rel / tiles_e);
+    const int mt = static_cast<int>(rel - static_cast<int64_t>(nt) * tiles_e);
+    const int n_e = s_off[e + 1] - s_off[e];
+    const int base = n_e / tiles_e, extra = n_e % tiles_e;
+    e_out = e;
+    nt_out = nt;
+    row0_out = s_off[e] + mt * base + (mt < extra ? mt : extra);
+    rows_out = base + (mt < extra ? 1 : 0);
+    return true;
+}
 
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
 __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
@@ -78,56 +149,8 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     const int lane = tid & 63;
     const int wave = tid >> 6;
 
-    // ---- tile schedule from expert_offsets ----
-    const int E = a.E;
-    for (int e = tid; e <= E; e += kThreads) {
-        int64_t o = a.offsets[e];
-        o = o < 0 ? 0 : (o > a.P ? a.P : o);
-        s_off[e] = static_cast<int32_t>(o);
-    }
-    __syncthreads();
-    {
-        int cnt = 0;
-        if (tid < E) {
-            const int n = s_off[tid + 1] - s_off[tid];
-            cnt = n > 0 ? (n + BM - 1) / BM : 0;
-        }
-        s_tstart[tid] = cnt;  // kThreads == kMaxE
-        __syncthreads();
-        for (int d = 1; d < kThreads; d <<= 1) {
-            const int v = tid >= d ? s_tstart[tid - d] : 0;
-            __syncthreads();
-            s_tstart[tid] += v;
-            __syncthreads();
-        }
-        // inclusive -> exclusive, s_tstart[E] = total
-        const int incl = s_tstart[tid];
-        __syncthreads();
-        s_tstart[tid + 1] = incl;
-        if (tid == 0) s_tstart[0] = 0;
-        __syncthreads();
-    }
-    const int NT = a.N / BN_OUT;
-    const int64_t total = static_cast<int64_t>(s_tstart[E]) * NT;
-    const int xcd = blockIdx.x % kNumXcd;
-    const int64_t local = blockIdx.x / kNumXcd;
-    const int64_t per = total / kNumXcd, rem = total % kNumXcd;
-    const int64_t cnt = per + (xcd < rem ? 1 : 0);
-    if (local >= cnt) return;  // uniform over the workgroup
-    const int64_t L = xcd * per + (xcd < rem ? xcd : rem) + local;
-    // expert: last e with s_tstart[e] * NT <= L
-    int lo = 0, hi = E - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (static_cast<int64_t>(s_tstart[mid]) * NT <= L) lo = mid; else hi = mid - 1;
-    }
-    const int e = lo;
-    const int tiles_e = s_tstart[e + 1] - s_tstart[e];
-    const int64_t rel = L - static_cast<int64_t>(s_tstart[e]) * NT;
-    const int nt = static_cast<int>(rel / tiles_e);
-    const int mt = static_cast<int>(rel - static_cast<int64_t>(nt) * tiles_e);
-    const int row0 = s_off[e] + mt * BM;
-    const int rows = min(BM, s_off[e + 1] - row0);
+    int e, nt, row0, rows;
+    if (!find_tile<BM>(a, a.N / BN_OUT, s_off, s_tstart, e, nt, row0, rows)) return;
     const int n0 = nt * BN_OUT;
     const int K = a.K;
 
@@ -253,6 +276,241 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     }
 }
 
+// Large-tile variant for experts with many rows (prefill and longer).
+//
+// 32x32x16 MFMA; a 256-thread workgroup owns a BM x BN tile and each of its 4
+// waves a (BM/WAVES_M) x (BN/WAVES_N) sub-tile, 256 fp32 accumulators per lane
+// at the 256x256 / 2x2 shape.  Row blocks of 32 go to the M-waves cyclically
+// (block b to wave b % WAVES_M) and blocks past the tile's last row are
+// skipped, so a partly filled tile costs MFMA time in proportion to its rows.
+// K advances 64 at a time through two LDS buffers.  Weight tiles (the HBM
+// stream) are loaded two stages ahead into two register sets, activation
+// tiles (mostly L2 hits) one stage ahead; K must be a multiple of 128.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
+__global__ __launch_bounds__(kThreads) void ffn_gemm32_kernel(FfnArgs a) {
+    static_assert(WAVES_M * WAVES_N == kWaves, "4 waves");
+    constexpr int BN_OUT = GATEUP ? BN / 2 : BN;
+    constexpr int MBLK = BM / 32;                    // row blocks per tile
+    constexpr int MB = MBLK / WAVES_M;               // row blocks per wave
+    constexpr int WN_OUT = BN_OUT / WAVES_N;
+    constexpr int NB = WN_OUT / 32;
+    constexpr int NACC = GATEUP ? 2 : 1;
+    static_assert(MB >= 1 && NB >= 1 && MBLK % WAVES_M == 0, "tile shape");
+    constexpr int A_ITERS = BM * (BK / 8) / kThreads;  // 16-byte chunks per thread
+    constexpr int B_ITERS = BN * (BK / 8) / kThreads;
+    static_assert(A_ITERS * kThreads == BM * (BK / 8) && B_ITERS * kThreads == BN * (BK / 8), "");
+    // chunk i of a thread covers tile row (tid / 8) + 32 * i: one 32-row block
+    static_assert(kThreads / 8 == 32, "loader row mapping");
+
+    __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * LDS_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint16_t s_b[2][BN * LDS_STRIDE];
+    __shared__ int32_t s_off[kMaxE + 1];
+    __shared__ int32_t s_tstart[kMaxE + 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    int e, nt, row0, rows;
+    if (!find_tile<BM>(a, a.N / BN_OUT, s_off, s_tstart, e, nt, row0, rows)) return;
+    const int n0 = nt * BN_OUT;
+    const int K = a.K;
+    const int nblk = (rows + 31) >> 5;  // row blocks holding at least one row
+
+    // ---- loader addressing: buffer loads, 32-bit per-lane offsets ----
+    // Thread t loads 16-byte chunk (t % 8) of tile rows (t / 8) + 32 i; chunk
+    // i of a thread therefore lies in row block i.  Uniform parts of every
+    // offset (row block, K stage) go in the scalar offset.
+    const int lrow = tid >> 3, lcol = (tid & 7) * 8;
+    __amdgpu_buffer_rsrc_t rsrc_a, rsrc_b0, rsrc_b1;
+    uint32_t a_off[GATEUP ? A_ITERS : 1];
+    uint32_t a_soff_blk = 0;  // bytes between row blocks of A (down: 32 rows of h)
+    if constexpr (GATEUP) {
+        // rows of x gathered through sorted_pairs; x is [T, K]
+        rsrc_a = make_rsrc(a.a_src, static_cast<uint32_t>(a.T * K * 2));
+#pragma unroll
+        for (int i = 0; i < A_ITERS; ++i) {
+            const int r = min(lrow + 32 * i, rows - 1);
+            int64_t tok = a.sorted_pairs[row0 + r] / a.k;
+            tok = tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
+            a_off[i] = static_cast<uint32_t>((tok * K + lcol) * 2);
+        }
+    } else {
+        // rows of h are the tile's own rows, contiguous from row0
+        rsrc_a = make_rsrc(a.a_src + static_cast<int64_t>(row0) * K,
+                           static_cast<uint32_t>(rows * K * 2));
+        a_off[0] = static_cast<uint32_t>((lrow * K + lcol) * 2);
+        a_soff_blk = static_cast<uint32_t>(32 * K * 2);
+    }
+    // weight rows of the tile: [n0, n0 + BN_OUT) of w_gate / w_up (gate/up) or
+    // of w_down (down), each K long
+    {
+        const int64_t first = (static_cast<int64_t>(e) * a.N + n0) * K;
+        rsrc_b0 = make_rsrc(a.b0 + first, static_cast<uint32_t>(BN_OUT * K * 2));
+        rsrc_b1 = GATEUP ? make_rsrc(a.b1 + first, static_cast<uint32_t>(BN_OUT * K * 2)) : rsrc_b0;
+    }
+    const uint32_t b_off = static_cast<uint32_t>((lrow * K + lcol) * 2);
+    const uint32_t b_soff_blk = static_cast<uint32_t>(32 * K * 2);
+
+    u32x4 ra[A_ITERS], rb[B_ITERS], rb2[B_ITERS];
+    auto load_a = [&](int kt) {
+        const uint32_t kbytes = static_cast<uint32_t>(kt * BK * 2);
+#pragma unroll
+        for (int i = 0; i < A_ITERS; ++i) {
+            if (i < nblk) {
+                if constexpr (GATEUP)
+                    ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[i], kbytes, 0);
+                else
+                    ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[0],
+                                                                  kbytes + i * a_soff_blk, 0);
+            }
+        }
+    };
+    auto load_b = [&](u32x4 (&rbx)[B_ITERS], int kt) {
+        const uint32_t kbytes = static_cast<uint32_t>(kt * BK * 2);
+#pragma unroll
+        for (int i = 0; i < B_ITERS; ++i) {
+            constexpr int HALF_ITERS = GATEUP ? B_ITERS / 2 : B_ITERS;
+            const int ib = i % HALF_ITERS;
+            rbx[i] = __builtin_amdgcn_raw_buffer_load_b128(i < HALF_ITERS ? rsrc_b0 : rsrc_b1, b_off,
+                                                          kbytes + ib * b_soff_blk, 0);
+        }
+    };
+    auto load_global = [&](u32x4 (&ra)[A_ITERS], u32x4 (&rb)[B_ITERS], int kt) {
+        const uint32_t kbytes = static_cast<uint32_t>(kt * BK * 2);
+#pragma unroll
+        for (int i = 0; i < A_ITERS; ++i) {
+            if (i < nblk) {
+                if constexpr (GATEUP)
+                    ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[i], kbytes, 0);
+                else
+                    ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[0],
+                                                                  kbytes + i * a_soff_blk, 0);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < B_ITERS; ++i) {
+            constexpr int HALF_ITERS = GATEUP ? B_ITERS / 2 : B_ITERS;
+            const int ib = i % HALF_ITERS;
+            rb[i] = __builtin_amdgcn_raw_buffer_load_b128(i < HALF_ITERS ? rsrc_b0 : rsrc_b1, b_off,
+                                                          kbytes + ib * b_soff_blk, 0);
+        }
+    };
+    auto store_lds = [&](const u32x4 (&ra)[A_ITERS], const u32x4 (&rb)[B_ITERS], int buf) {
+#pragma unroll
+        for (int i = 0; i < A_ITERS; ++i)
+            if (i < nblk)
+                *reinterpret_cast<u32x4*>(&s_a[buf][(lrow + 32 * i) * LDS_STRIDE + lcol]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_ITERS; ++i)
+            *reinterpret_cast<u32x4*>(&s_b[buf][(lrow + 32 * i) * LDS_STRIDE + lcol]) = rb[i];
+    };
+
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int r32 = lane & 31, half = lane >> 5;
+    int mb_valid = 0;  // this wave's blocks wm, wm + WAVES_M, ... below nblk
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) mb_valid += (wm + WAVES_M * mb) < nblk;
+
+    f32x16 acc[NACC][MB][NB];
+#pragma unroll
+    for (int g = 0; g < NACC; ++g)
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[g][m][n][i] = 0.0f;
+
+    // The K loop is compiled once per count NV of valid row blocks of this
+    // wave, so its MFMA sequence has no branches.
+    auto k_loop = [&](auto nv_tag) {
+        constexpr int NV = decltype(nv_tag)::value;
+        auto compute = [&](int buf) {
+            const uint16_t* sa = s_a[buf];
+            const uint16_t* sb = s_b[buf];
+#pragma unroll
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                const int kof = ks * 16 + half * 8;
+                bf16x8 af[NV > 0 ? NV : 1];
+#pragma unroll
+                for (int m = 0; m < NV; ++m)
+                    af[m] = *reinterpret_cast<const bf16x8*>(
+                        &sa[((wm + WAVES_M * m) * 32 + r32) * LDS_STRIDE + kof]);
+#pragma unroll
+                for (int g = 0; g < NACC; ++g) {
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) {
+                        if constexpr (NV > 0) {
+                            const int brow = g * BN_OUT + wn * WN_OUT + n * 32 + r32;
+                            const bf16x8 bfr =
+                                *reinterpret_cast<const bf16x8*>(&sb[brow * LDS_STRIDE + kof]);
+#pragma unroll
+                            for (int m = 0; m < NV; ++m)
+                                acc[g][m][n] = mfma32(af[m], bfr, acc[g][m][n]);
+                        }
+                    }
+                }
+            }
+        };
+        // nk is even (K % 128 == 0).  Weights run two stages ahead in two
+        // register sets, activations one stage ahead; the loop is unrolled by
+        // two so the register sets never move.  Past the end, loads repeat the
+        // last stage and the store fills the buffer nobody reads.
+        const int nk = K / BK;
+        load_a(0);
+        load_b(rb, 0);
+        load_b(rb2, 1);
+        store_lds(ra, rb, 0);
+        __syncthreads();
+        for (int kt = 0; kt < nk; kt += 2) {
+            load_a(kt + 1);
+            load_b(rb, kt + 2 < nk ? kt + 2 : nk - 1);
+            compute(0);
+            store_lds(ra, rb2, 1);
+            __syncthreads();
+            load_a(kt + 2 < nk ? kt + 2 : nk - 1);
+            load_b(rb2, kt + 3 < nk ? kt + 3 : nk - 1);
+            compute(1);
+            store_lds(ra, rb, 0);
+            __syncthreads();
+        }
+    };
+    static_assert(MB <= 4, "k_loop dispatch covers up to 4 blocks per wave");
+    switch (mb_valid) {
+        case 0: k_loop(std::integral_constant<int, 0>{}); break;
+        case 1: k_loop(std::integral_constant<int, 1>{}); break;
+        case 2: k_loop(std::integral_constant<int, (MB >= 2 ? 2 : 1)>{}); break;
+        case 3: k_loop(std::integral_constant<int, (MB >= 3 ? 3 : 1)>{}); break;
+        default: k_loop(std::integral_constant<int, MB>{}); break;
+    }
+
+    // ---- epilogue ----
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+        if (m >= mb_valid) continue;
+        const int blk = wm + WAVES_M * m;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int r = blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (r >= rows) continue;
+            const int64_t orow = row0 + r;
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                const int col = n0 + wn * WN_OUT + n * 32 + r32;
+                if constexpr (GATEUP) {
+                    const float g = acc[0][m][n][i];
+                    const float u = acc[1][m][n][i];
+                    const float prod = (g * sigmoid_f32(g)) * u;
+                    static_cast<uint16_t*>(a.out)[orow * a.N + col] = f32_to_bf16_rne(prod);
+                } else {
+                    static_cast<float*>(a.out)[orow * a.N + col] = acc[0][m][n][i];
+                }
+            }
+        }
+    }
+}
+
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
 hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
     constexpr int BN_OUT = GATEUP ? BN / 2 : BN;
@@ -266,30 +524,53 @@ hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
+hipError_t launch_gemm32(const FfnArgs& a, hipStream_t s) {
+    constexpr int BN_OUT = GATEUP ? BN / 2 : BN;
+    const int64_t mtiles = (a.P + BM - 1) / BM + (a.E < a.P ? a.E : a.P);
+    const int64_t tiles = mtiles * (a.N / BN_OUT);
+    const int64_t grid = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    ffn_gemm32_kernel<BM, BN, WAVES_M, WAVES_N, GATEUP>
+        <<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s>>>(a);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* sorted_pairs,
+                          const int32_t* offsets, const uint16_t* w_gate, const uint16_t* w_up,
+                          uint16_t* h, hipStream_t s) {
+    const int64_t P = p.T * p.k;
+    const FfnArgs a{P, p.T, p.k, p.E, p.H, p.I, x, sorted_pairs, offsets, w_gate, w_up, h};
+    const int64_t rows_per_expert = P / p.E;
+    if (rows_per_expert <= 24) return launch_gemm<16, 128, 1, 4, true>(a, s);
+    // the large-tile kernel addresses x with 32-bit buffer offsets
+    const bool x_fits = p.T * static_cast<int64_t>(p.H) * 2 < (static_cast<int64_t>(1) << 31);
+    if (rows_per_expert <= 96 || p.I % 128 != 0 || !x_fits)
+        return launch_gemm<64, 128, 1, 4, true>(a, s);
+    return launch_gemm32<256, 256, 2, 2, true>(a, s);
+}
+
+hipError_t launch_down(const Problem& p, const uint16_t* h, const int32_t* offsets,
+                       const uint16_t* w_down, float* y, hipStream_t s) {
+    const int64_t P = p.T * p.k;
+    const FfnArgs a{P, p.T, p.k, p.E, p.I, p.H, h, nullptr, offsets, w_down, nullptr, y};
+    const int64_t rows_per_expert = P / p.E;
+    if (rows_per_expert <= 24) return launch_gemm<16, 64, 1, 4, false>(a, s);
+    if (rows_per_expert <= 96 || p.H % 256 != 0 || p.I % 128 != 0)
+        return launch_gemm<64, 128, 1, 4, false>(a, s);
+    return launch_gemm32<256, 256, 2, 2, false>(a, s);
+}
 
 hipError_t launch_expert_ffn(const Problem& p, const uint16_t* x, const int32_t* sorted_pairs,
                              const int32_t* offsets, const uint16_t* w_gate,
                              const uint16_t* w_up, const uint16_t* w_down, uint16_t* h, float* y,
                              hipStream_t s) {
-    const int64_t P = p.T * p.k;
-    FfnArgs gu{P, p.T, p.k, p.E, p.H, p.I, x, sorted_pairs, offsets, w_gate, w_up, h};
-    FfnArgs dn{P, p.T, p.k, p.E, p.I, p.H, h, sorted_pairs, offsets, w_down, nullptr, y};
-    const int64_t rows_per_expert = P / p.E;
-    hipError_t err;
-    if (rows_per_expert <= 24) {
-        err = launch_gemm<16, 128, 1, 4, true>(gu, s);
-        if (err != hipSuccess) return err;
-        return launch_gemm<16, 64, 1, 4, false>(dn, s);
-    }
-    if (rows_per_expert <= 96) {
-        err = launch_gemm<64, 128, 1, 4, true>(gu, s);
-        if (err != hipSuccess) return err;
-        return launch_gemm<64, 128, 1, 4, false>(dn, s);
-    }
-    err = launch_gemm<128, 128, 2, 2, true>(gu, s);
+    const hipError_t err = launch_gate_up(p, x, sorted_pairs, offsets, w_gate, w_up, h, s);
     if (err != hipSuccess) return err;
-    return launch_gemm<128, 128, 2, 2, false>(dn, s);
+    return launch_down(p, h, offsets, w_down, y, s);
 }
 
 }  // namespace moe

@@ -31,6 +31,13 @@ hipError_t launch_expert_ffn(const Problem& p, const uint16_t* x, const int32_t*
                              const uint16_t* w_up, const uint16_t* w_down, uint16_t* h, float* y,
                              hipStream_t s);
 
+hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* sorted_pairs,
+                          const int32_t* offsets, const uint16_t* w_gate, const uint16_t* w_up,
+                          uint16_t* h, hipStream_t s);
+
+hipError_t launch_down(const Problem& p, const uint16_t* h, const int32_t* offsets,
+                       const uint16_t* w_down, float* y, hipStream_t s);
+
 hipError_t launch_combine(const Problem& p, const float* y, const int32_t* pair_rows,
                           const float* weights, void* out, bool out_bf16, hipStream_t s);
 

@@ -182,6 +182,36 @@ MOE_EXPORT moe_status moe_expert_ffn(const moe_problem* p, const moe_bf16* x,
                       "expert ffn launch");
 }
 
+MOE_EXPORT moe_status moe_expert_gate_up(const moe_problem* p, const moe_bf16* x,
+                                         const int32_t* sorted_pairs,
+                                         const int32_t* expert_offsets, const moe_bf16* w_gate,
+                                         const moe_bf16* w_up, moe_bf16* h, hipStream_t stream) {
+    MOE_TRY(check_problem(p));
+    if (p->T == 0) return ok();
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(sorted_pairs, "sorted_pairs"));
+    MOE_TRY(check_ptr(expert_offsets, "expert_offsets"));
+    MOE_TRY(check_ptr(w_gate, "w_gate"));
+    MOE_TRY(check_ptr(w_up, "w_up"));
+    MOE_TRY(check_ptr(h, "h"));
+    return hip_status(moe::launch_gate_up(to_internal(*p), x, sorted_pairs, expert_offsets, w_gate,
+                                          w_up, h, stream),
+                      "gate/up launch");
+}
+
+MOE_EXPORT moe_status moe_expert_down(const moe_problem* p, const moe_bf16* h,
+                                      const int32_t* expert_offsets, const moe_bf16* w_down,
+                                      float* y, hipStream_t stream) {
+    MOE_TRY(check_problem(p));
+    if (p->T == 0) return ok();
+    MOE_TRY(check_ptr(h, "h"));
+    MOE_TRY(check_ptr(expert_offsets, "expert_offsets"));
+    MOE_TRY(check_ptr(w_down, "w_down"));
+    MOE_TRY(check_ptr(y, "y"));
+    return hip_status(moe::launch_down(to_internal(*p), h, expert_offsets, w_down, y, stream),
+                      "down launch");
+}
+
 MOE_EXPORT moe_status moe_combine(const moe_problem* p, const float* y, const int32_t* pair_rows,
                                   const float* topk_weights, void* out, moe_dtype out_dtype,
                                   hipStream_t stream) {

@@ -48,8 +48,9 @@ class MoEProblem(ctypes.Structure):
                    cfg.scale)
 
 
-EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn", "moe_combine",
-           "moe_forward", "moe_status_string", "moe_last_error")
+EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
+           "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward",
+           "moe_status_string", "moe_last_error")
 
 
 def library_path() -> str:
@@ -93,6 +94,10 @@ def load_library():
         lib.moe_permute.restype = st
         lib.moe_expert_ffn.argtypes = [prob, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.moe_expert_ffn.restype = st
+        lib.moe_expert_gate_up.argtypes = [prob, P, P, P, P, P, P, P]
+        lib.moe_expert_gate_up.restype = st
+        lib.moe_expert_down.argtypes = [prob, P, P, P, P, P]
+        lib.moe_expert_down.restype = st
         lib.moe_combine.argtypes = [prob, P, P, P, P, ctypes.c_int, P]
         lib.moe_combine.restype = st
         lib.moe_forward.argtypes = [prob, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, P,
@@ -160,6 +165,17 @@ def moe_expert_ffn(p, x, sorted_pairs, expert_offsets, w_gate, w_up, w_down, y, 
                                           _p(y), _p(ws), nbytes, _stream(stream)))
 
 
+def moe_expert_gate_up(p, x, sorted_pairs, expert_offsets, w_gate, w_up, h, stream=None):
+    _check(load_library().moe_expert_gate_up(ctypes.byref(p), _p(x), _p(sorted_pairs),
+                                              _p(expert_offsets), _p(w_gate), _p(w_up), _p(h),
+                                              _stream(stream)))
+
+
+def moe_expert_down(p, h, expert_offsets, w_down, y, stream=None):
+    _check(load_library().moe_expert_down(ctypes.byref(p), _p(h), _p(expert_offsets),
+                                           _p(w_down), _p(y), _stream(stream)))
+
+
 def moe_combine(p, y, pair_rows, topk_weights, out, stream=None):
     _check(load_library().moe_combine(ctypes.byref(p), _p(y), _p(pair_rows), _p(topk_weights),
                                        _p(out), _dtype_code(out), _stream(stream)))
@@ -188,5 +204,6 @@ def alloc_buffers(p: MoEProblem, device="cuda", out_dtype=torch.float32):
         sorted_pairs=torch.empty((T * k,), dtype=torch.int32, device=device),
         pair_rows=torch.empty((T * k,), dtype=torch.int32, device=device),
         y=torch.empty((T * k, H), dtype=torch.float32, device=device),
+        h=torch.empty((T * k, p.I), dtype=torch.bfloat16, device=device),
         ws=torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=device),
     )

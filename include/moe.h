@@ -119,6 +119,20 @@ moe_status moe_expert_ffn(const moe_problem* p, const moe_bf16* x, const int32_t
                           const moe_bf16* w_up, const moe_bf16* w_down, float* y, void* ws,
                           size_t ws_bytes, hipStream_t stream);
 
+/* The two halves of moe_expert_ffn, for callers that keep h themselves.
+ *   moe_expert_gate_up:  h [T*k,I] bf16 out (sorted order),
+ *       h[q] = bf16(silu(x_q . w_gate[e]^T) * (x_q . w_up[e]^T)),
+ *       x_q = x[sorted_pairs[q] / k], e the expert owning position q.
+ *   moe_expert_down:     y [T*k,H] fp32 out, y[q] = h[q] . w_down[e]^T.
+ * Same layouts, tile schedule and rounding as moe_expert_ffn, which is
+ * exactly these two calls with h in the workspace.  No workspace needed. */
+moe_status moe_expert_gate_up(const moe_problem* p, const moe_bf16* x, const int32_t* sorted_pairs,
+                              const int32_t* expert_offsets, const moe_bf16* w_gate,
+                              const moe_bf16* w_up, moe_bf16* h, hipStream_t stream);
+
+moe_status moe_expert_down(const moe_problem* p, const moe_bf16* h, const int32_t* expert_offsets,
+                           const moe_bf16* w_down, float* y, hipStream_t stream);
+
 /* Weighted recombination without atomics.
  *   y            [T*k,H] fp32 in sorted order
  *   pair_rows    [T*k] int32 (from moe_permute); -1 entries contribute 0

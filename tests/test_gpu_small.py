@@ -97,6 +97,8 @@ SHAPES = [
     (1000, 256, 128, 32, 4, 2, 2),
     (3000, 256, 128, 16, 4, 2, 4),
     (5000, 128, 64, 16, 4, 2, 4),
+    (2000, 512, 256, 8, 2, 1, 2),       # ~500 rows per expert: two large row tiles
+    (1500, 256, 384, 16, 4, 2, 4),      # ~375 rows per expert, I not a power of two
 ]
 
 
