@@ -48,6 +48,15 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                              static_cast<int>(bytes), 0x00020000);
 }
 
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_for<B + 1, E>(f);
+    }
+}
+
 struct FfnArgs {
     int64_t P;       // pairs (rows of h and y)
     int64_t T;       // tokens (rows of x)
@@ -320,11 +329,13 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm32_kernel(FfnArgs a) {
     // ---- loader addressing: buffer loads, 32-bit per-lane offsets ----
     // Thread t loads 16-byte chunk (t % 8) of tile rows (t / 8) + 32 i; chunk
     // i of a thread therefore lies in row block i.  Uniform parts of every
-    // offset (row block, K stage) go in the scalar offset.
+    // offset (row block, K stage) go in the scalar offset.  Row blocks past
+    // the tile's rows get an offset outside the buffer, so their loads return
+    // zero without touching memory and the stage body has no branches.
     const int lrow = tid >> 3, lcol = (tid & 7) * 8;
+    constexpr uint32_t kOutside = 0x80000000u;  // beyond every buffer used here
     __amdgpu_buffer_rsrc_t rsrc_a, rsrc_b0, rsrc_b1;
-    uint32_t a_off[GATEUP ? A_ITERS : 1];
-    uint32_t a_soff_blk = 0;  // bytes between row blocks of A (down: 32 rows of h)
+    uint32_t a_off[A_ITERS];
     if constexpr (GATEUP) {
         // rows of x gathered through sorted_pairs; x is [T, K]
         rsrc_a = make_rsrc(a.a_src, static_cast<uint32_t>(a.T * K * 2));
@@ -333,14 +344,15 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm32_kernel(FfnArgs a) {
             const int r = min(lrow + 32 * i, rows - 1);
             int64_t tok = a.sorted_pairs[row0 + r] / a.k;
             tok = tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
-            a_off[i] = static_cast<uint32_t>((tok * K + lcol) * 2);
+            a_off[i] = i < nblk ? static_cast<uint32_t>((tok * K + lcol) * 2) : kOutside;
         }
     } else {
         // rows of h are the tile's own rows, contiguous from row0
         rsrc_a = make_rsrc(a.a_src + static_cast<int64_t>(row0) * K,
                            static_cast<uint32_t>(rows * K * 2));
-        a_off[0] = static_cast<uint32_t>((lrow * K + lcol) * 2);
-        a_soff_blk = static_cast<uint32_t>(32 * K * 2);
+#pragma unroll
+        for (int i = 0; i < A_ITERS; ++i)
+            a_off[i] = i < nblk ? static_cast<uint32_t>(((lrow + 32 * i) * K + lcol) * 2) : kOutside;
     }
     // weight rows of the tile: [n0, n0 + BN_OUT) of w_gate / w_up (gate/up) or
     // of w_down (down), each K long
@@ -356,54 +368,24 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm32_kernel(FfnArgs a) {
     auto load_a = [&](int kt) {
         const uint32_t kbytes = static_cast<uint32_t>(kt * BK * 2);
 #pragma unroll
-        for (int i = 0; i < A_ITERS; ++i) {
-            if (i < nblk) {
-                if constexpr (GATEUP)
-                    ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[i], kbytes, 0);
-                else
-                    ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[0],
-                                                                  kbytes + i * a_soff_blk, 0);
-            }
-        }
+        for (int i = 0; i < A_ITERS; ++i)
+            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[i], kbytes, 0);
     };
     auto load_b = [&](u32x4 (&rbx)[B_ITERS], int kt) {
         const uint32_t kbytes = static_cast<uint32_t>(kt * BK * 2);
-#pragma unroll
-        for (int i = 0; i < B_ITERS; ++i) {
-            constexpr int HALF_ITERS = GATEUP ? B_ITERS / 2 : B_ITERS;
-            const int ib = i % HALF_ITERS;
-            rbx[i] = __builtin_amdgcn_raw_buffer_load_b128(i < HALF_ITERS ? rsrc_b0 : rsrc_b1, b_off,
-                                                          kbytes + ib * b_soff_blk, 0);
-        }
-    };
-    auto load_global = [&](u32x4 (&ra)[A_ITERS], u32x4 (&rb)[B_ITERS], int kt) {
-        const uint32_t kbytes = static_cast<uint32_t>(kt * BK * 2);
-#pragma unroll
-        for (int i = 0; i < A_ITERS; ++i) {
-            if (i < nblk) {
-                if constexpr (GATEUP)
-                    ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[i], kbytes, 0);
-                else
-                    ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[0],
-                                                                  kbytes + i * a_soff_blk, 0);
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < B_ITERS; ++i) {
-            constexpr int HALF_ITERS = GATEUP ? B_ITERS / 2 : B_ITERS;
-            const int ib = i % HALF_ITERS;
-            rb[i] = __builtin_amdgcn_raw_buffer_load_b128(i < HALF_ITERS ? rsrc_b0 : rsrc_b1, b_off,
-                                                          kbytes + ib * b_soff_blk, 0);
-        }
-    };
-    auto store_lds = [&](const u32x4 (&ra)[A_ITERS], const u32x4 (&rb)[B_ITERS], int buf) {
-#pragma unroll
-        for (int i = 0; i < A_ITERS; ++i)
-            if (i < nblk)
-                *reinterpret_cast<u32x4*>(&s_a[buf][(lrow + 32 * i) * LDS_STRIDE + lcol]) = ra[i];
+        constexpr int HALF_ITERS = GATEUP ? B_ITERS / 2 : B_ITERS;
 #pragma unroll
         for (int i = 0; i < B_ITERS; ++i)
-            *reinterpret_cast<u32x4*>(&s_b[buf][(lrow + 32 * i) * LDS_STRIDE + lcol]) = rb[i];
+            rbx[i] = __builtin_amdgcn_raw_buffer_load_b128(i < HALF_ITERS ? rsrc_b0 : rsrc_b1, b_off,
+                                                           kbytes + (i % HALF_ITERS) * b_soff_blk, 0);
+    };
+    auto store_lds = [&](const u32x4 (&rbx)[B_ITERS], int buf) {
+#pragma unroll
+        for (int i = 0; i < A_ITERS; ++i)
+            *reinterpret_cast<u32x4*>(&s_a[buf][(lrow + 32 * i) * LDS_STRIDE + lcol]) = ra[i];
+#pragma unroll
+        for (int i = 0; i < B_ITERS; ++i)
+            *reinterpret_cast<u32x4*>(&s_b[buf][(lrow + 32 * i) * LDS_STRIDE + lcol]) = rbx[i];
     };
 
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -423,57 +405,114 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm32_kernel(FfnArgs a) {
                 for (int i = 0; i < 16; ++i) acc[g][m][n][i] = 0.0f;
 
     // The K loop is compiled once per count NV of valid row blocks of this
-    // wave, so its MFMA sequence has no branches.
+    // wave, so its MFMA sequence has no branches.  Within a stage the operand
+    // fragments of k-substep s+1 are read from LDS while the MFMAs of substep
+    // s run (two fragment register sets), the global loads of later stages are
+    // issued under the first substep, and the LDS stores of the next stage go
+    // under the last one.
     auto k_loop = [&](auto nv_tag) {
         constexpr int NV = decltype(nv_tag)::value;
-        auto compute = [&](int buf) {
+        constexpr int NA = NV > 0 ? NV : 1;
+        struct Frags {
+            bf16x8 a[NA];
+            bf16x8 b[NACC * NB];
+        };
+        auto load_frags = [&](Frags& f, int buf, int ks) {
             const uint16_t* sa = s_a[buf];
             const uint16_t* sb = s_b[buf];
+            const int kof = ks * 16 + half * 8;
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                const int kof = ks * 16 + half * 8;
-                bf16x8 af[NV > 0 ? NV : 1];
+            for (int m = 0; m < NV; ++m)
+                f.a[m] = *reinterpret_cast<const bf16x8*>(
+                    &sa[((wm + WAVES_M * m) * 32 + r32) * LDS_STRIDE + kof]);
+            if constexpr (NV > 0) {
 #pragma unroll
-                for (int m = 0; m < NV; ++m)
-                    af[m] = *reinterpret_cast<const bf16x8*>(
-                        &sa[((wm + WAVES_M * m) * 32 + r32) * LDS_STRIDE + kof]);
+                for (int g = 0; g < NACC; ++g)
 #pragma unroll
-                for (int g = 0; g < NACC; ++g) {
-#pragma unroll
-                    for (int n = 0; n < NB; ++n) {
-                        if constexpr (NV > 0) {
-                            const int brow = g * BN_OUT + wn * WN_OUT + n * 32 + r32;
-                            const bf16x8 bfr =
-                                *reinterpret_cast<const bf16x8*>(&sb[brow * LDS_STRIDE + kof]);
-#pragma unroll
-                            for (int m = 0; m < NV; ++m)
-                                acc[g][m][n] = mfma32(af[m], bfr, acc[g][m][n]);
-                        }
-                    }
-                }
+                    for (int n = 0; n < NB; ++n)
+                        f.b[g * NB + n] = *reinterpret_cast<const bf16x8*>(
+                            &sb[(g * BN_OUT + wn * WN_OUT + n * 32 + r32) * LDS_STRIDE + kof]);
             }
+        };
+        auto mfmas = [&](const Frags& f) {
+#pragma unroll
+            for (int g = 0; g < NACC; ++g)
+#pragma unroll
+                for (int n = 0; n < NB; ++n)
+#pragma unroll
+                    for (int m = 0; m < NV; ++m)
+                        acc[g][m][n] = mfma32(f.a[m], f.b[g * NB + n], acc[g][m][n]);
+        };
+        // one K stage from LDS buffer `buf`.
+        // Program order lists each group of work once; the scheduling-group
+        // fences at the end then spread the global loads, the fragment reads
+        // of the next substep and the LDS stores of the next stage between the
+        // MFMAs, so the MFMA unit is fed while the memory pipes work.
+        auto stage = [&](Frags& f0, Frags& f1, int buf, int ka, int kb, u32x4 (&rb_load)[B_ITERS],
+                         const u32x4 (&rb_store)[B_ITERS]) {
+            load_frags(f0, buf, 0);
+            load_a(ka);
+            load_b(rb_load, kb);
+            load_frags(f1, buf, 1);
+            mfmas(f0);
+            load_frags(f0, buf, 2);
+            mfmas(f1);
+            load_frags(f1, buf, 3);
+            mfmas(f0);
+            store_lds(rb_store, buf ^ 1);
+            mfmas(f1);
+            if constexpr (NV > 0) {
+                constexpr int MF = NV * NACC * NB;          // MFMAs per substep
+                constexpr int FR = NV + NACC * NB;          // fragment reads per substep
+                constexpr int VM = A_ITERS + B_ITERS;       // global loads per stage
+                constexpr int WR = A_ITERS + B_ITERS;       // LDS stores per stage
+                constexpr int VM0 = (VM + 1) / 2;           // loads under substep 0
+                // fragments of substep 0 first (nothing to overlap them with)
+                __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
+                // substep 0: fragments of substep 1 and the first half of the loads
+                static_for<0, MF>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if constexpr (i < FR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if constexpr (i < VM0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                });
+                // substep 1: fragments of substep 2 and the rest of the loads
+                static_for<0, MF>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if constexpr (i < FR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if constexpr (i < VM - VM0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                });
+                // substep 2: fragments of substep 3
+                static_for<0, MF>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if constexpr (i < FR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                });
+                // substep 3: the LDS stores of the next stage
+                static_for<0, MF>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    constexpr int n = (i + 1) * WR / MF - i * WR / MF;
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x200, n, 0);
+                });
+            }
+            __syncthreads();
         };
         // nk is even (K % 128 == 0).  Weights run two stages ahead in two
         // register sets, activations one stage ahead; the loop is unrolled by
         // two so the register sets never move.  Past the end, loads repeat the
         // last stage and the store fills the buffer nobody reads.
         const int nk = K / BK;
+        Frags f0, f1;
         load_a(0);
         load_b(rb, 0);
         load_b(rb2, 1);
-        store_lds(ra, rb, 0);
+        store_lds(rb, 0);
         __syncthreads();
         for (int kt = 0; kt < nk; kt += 2) {
-            load_a(kt + 1);
-            load_b(rb, kt + 2 < nk ? kt + 2 : nk - 1);
-            compute(0);
-            store_lds(ra, rb2, 1);
-            __syncthreads();
-            load_a(kt + 2 < nk ? kt + 2 : nk - 1);
-            load_b(rb2, kt + 3 < nk ? kt + 3 : nk - 1);
-            compute(1);
-            store_lds(ra, rb, 0);
-            __syncthreads();
+            stage(f0, f1, 0, kt + 1, kt + 2 < nk ? kt + 2 : nk - 1, rb, rb2);
+            stage(f0, f1, 1, kt + 2 < nk ? kt + 2 : nk - 1, kt + 3 < nk ? kt + 3 : nk - 1, rb2, rb);
         }
     };
     static_assert(MB <= 4, "k_loop dispatch covers up to 4 blocks per wave");

@@ -9,7 +9,7 @@
 
 #include <string>
 
-#include "../../include/moe.h"
+#include "moe.h"
 #include "kernels.h"
 
 #define MOE_EXPORT extern "C" __attribute__((visibility("default")))
