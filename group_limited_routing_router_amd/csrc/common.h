@@ -31,6 +31,13 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
 
 __device__ __forceinline__ float sigmoid_f32(float z) { return 1.0f / (1.0f + expf(-z)); }
 
+// silu(z) = z * sigmoid(z) in fp32 with the hardware exp2 and reciprocal
+// (about 1 ulp each); the result is rounded to bf16 right after, so the
+// difference to correctly rounded fp32 shows only at bf16 rounding ties.
+__device__ __forceinline__ float silu_f32(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
+
 // One 16x16x32 bf16 MFMA step: acc += A(16x32) * B(32x16).  Lane l supplies
 // row (l % 16) of A and column (l % 16) of B, both for the 8 consecutive k of
 // chunk (l / 16); it receives rows 4*(l/16) .. 4*(l/16)+3 of column (l % 16).

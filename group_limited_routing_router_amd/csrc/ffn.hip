@@ -311,8 +311,13 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm32_kernel(FfnArgs a) {
     // chunk i of a thread covers tile row (tid / 8) + 32 * i: one 32-row block
     static_assert(kThreads / 8 == 32, "loader row mapping");
 
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint16_t s_b[2][BN * LDS_STRIDE];
+    // One LDS arena: two A and two B stage buffers during the K loop, then
+    // the output tile staged for wide stores in the epilogue.
+    constexpr int A_ELEMS = BM * LDS_STRIDE, B_ELEMS = BN * LDS_STRIDE;
+    constexpr int ARENA = 2 * (A_ELEMS + B_ELEMS);
+    __shared__ __attribute__((aligned(16))) uint16_t s_arena[ARENA];
+    uint16_t* const s_a[2] = {s_arena, s_arena + A_ELEMS};
+    uint16_t* const s_b[2] = {s_arena + 2 * A_ELEMS, s_arena + 2 * A_ELEMS + B_ELEMS};
     __shared__ int32_t s_off[kMaxE + 1];
     __shared__ int32_t s_tstart[kMaxE + 1];
 
@@ -364,12 +369,12 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm32_kernel(FfnArgs a) {
     const uint32_t b_off = static_cast<uint32_t>((lrow * K + lcol) * 2);
     const uint32_t b_soff_blk = static_cast<uint32_t>(32 * K * 2);
 
-    u32x4 ra[A_ITERS], rb[B_ITERS], rb2[B_ITERS];
-    auto load_a = [&](int kt) {
+    u32x4 ra[A_ITERS], ra2[A_ITERS], rb[B_ITERS], rb2[B_ITERS];
+    auto load_a = [&](u32x4 (&rax)[A_ITERS], int kt) {
         const uint32_t kbytes = static_cast<uint32_t>(kt * BK * 2);
 #pragma unroll
         for (int i = 0; i < A_ITERS; ++i)
-            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[i], kbytes, 0);
+            rax[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[i], kbytes, 0);
     };
     auto load_b = [&](u32x4 (&rbx)[B_ITERS], int kt) {
         const uint32_t kbytes = static_cast<uint32_t>(kt * BK * 2);
@@ -379,10 +384,10 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm32_kernel(FfnArgs a) {
             rbx[i] = __builtin_amdgcn_raw_buffer_load_b128(i < HALF_ITERS ? rsrc_b0 : rsrc_b1, b_off,
                                                            kbytes + (i % HALF_ITERS) * b_soff_blk, 0);
     };
-    auto store_lds = [&](const u32x4 (&rbx)[B_ITERS], int buf) {
+    auto store_lds = [&](const u32x4 (&rax)[A_ITERS], const u32x4 (&rbx)[B_ITERS], int buf) {
 #pragma unroll
         for (int i = 0; i < A_ITERS; ++i)
-            *reinterpret_cast<u32x4*>(&s_a[buf][(lrow + 32 * i) * LDS_STRIDE + lcol]) = ra[i];
+            *reinterpret_cast<u32x4*>(&s_a[buf][(lrow + 32 * i) * LDS_STRIDE + lcol]) = rax[i];
 #pragma unroll
         for (int i = 0; i < B_ITERS; ++i)
             *reinterpret_cast<u32x4*>(&s_b[buf][(lrow + 32 * i) * LDS_STRIDE + lcol]) = rbx[i];
@@ -448,18 +453,19 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm32_kernel(FfnArgs a) {
         // fences at the end then spread the global loads, the fragment reads
         // of the next substep and the LDS stores of the next stage between the
         // MFMAs, so the MFMA unit is fed while the memory pipes work.
-        auto stage = [&](Frags& f0, Frags& f1, int buf, int ka, int kb, u32x4 (&rb_load)[B_ITERS],
+        auto stage = [&](Frags& f0, Frags& f1, int buf, int kl, u32x4 (&ra_load)[A_ITERS],
+                         u32x4 (&rb_load)[B_ITERS], const u32x4 (&ra_store)[A_ITERS],
                          const u32x4 (&rb_store)[B_ITERS]) {
             load_frags(f0, buf, 0);
-            load_a(ka);
-            load_b(rb_load, kb);
+            load_a(ra_load, kl);
+            load_b(rb_load, kl);
             load_frags(f1, buf, 1);
             mfmas(f0);
             load_frags(f0, buf, 2);
             mfmas(f1);
             load_frags(f1, buf, 3);
             mfmas(f0);
-            store_lds(rb_store, buf ^ 1);
+            store_lds(ra_store, rb_store, buf ^ 1);
             mfmas(f1);
             if constexpr (NV > 0) {
                 constexpr int MF = NV * NACC * NB;          // MFMAs per substep
@@ -499,20 +505,23 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm32_kernel(FfnArgs a) {
             }
             __syncthreads();
         };
-        // nk is even (K % 128 == 0).  Weights run two stages ahead in two
-        // register sets, activations one stage ahead; the loop is unrolled by
-        // two so the register sets never move.  Past the end, loads repeat the
-        // last stage and the store fills the buffer nobody reads.
+        // nk is even (K % 128 == 0).  Global loads run two stages ahead in
+        // two register sets; the loop is unrolled by two so the sets never
+        // move.  Past the end, loads repeat the last stage and the store
+        // fills the buffer nobody reads.
         const int nk = K / BK;
         Frags f0, f1;
-        load_a(0);
+        load_a(ra, 0);
         load_b(rb, 0);
+        load_a(ra2, 1);
         load_b(rb2, 1);
-        store_lds(rb, 0);
+        store_lds(ra, rb, 0);
         __syncthreads();
         for (int kt = 0; kt < nk; kt += 2) {
-            stage(f0, f1, 0, kt + 1, kt + 2 < nk ? kt + 2 : nk - 1, rb, rb2);
-            stage(f0, f1, 1, kt + 2 < nk ? kt + 2 : nk - 1, kt + 3 < nk ? kt + 3 : nk - 1, rb2, rb);
+            const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;
+            const int k3 = kt + 3 < nk ? kt + 3 : nk - 1;
+            stage(f0, f1, 0, k2, ra, rb, ra2, rb2);
+            stage(f0, f1, 1, k3, ra2, rb2, ra, rb);
         }
     };
     static_assert(MB <= 4, "k_loop dispatch covers up to 4 blocks per wave");
@@ -524,28 +533,71 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm32_kernel(FfnArgs a) {
         default: k_loop(std::integral_constant<int, MB>{}); break;
     }
 
-    // ---- epilogue ----
+    // ---- epilogue: stage the output tile in LDS, then 16-byte stores ----
+    // (the K loop ended with a barrier, so the arena is free)
+    const int out_row0 = row0;
+    if constexpr (GATEUP) {
+        // h tile: rows x BN_OUT bf16, row stride BN_OUT + 8 (bank spread)
+        constexpr int HS = BN_OUT + 8;
+        static_assert(BM * HS <= ARENA, "h tile fits the arena");
+        uint16_t* s_h = s_arena;
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-        if (m >= mb_valid) continue;
-        const int blk = wm + WAVES_M * m;
+        for (int m = 0; m < MB; ++m) {
+            if (m >= mb_valid) continue;
+            const int blk = wm + WAVES_M * m;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int r = blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (r >= rows) continue;
-            const int64_t orow = row0 + r;
+            for (int i = 0; i < 16; ++i) {
+                const int r = blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
 #pragma unroll
-            for (int n = 0; n < NB; ++n) {
-                const int col = n0 + wn * WN_OUT + n * 32 + r32;
-                if constexpr (GATEUP) {
+                for (int n = 0; n < NB; ++n) {
                     const float g = acc[0][m][n][i];
                     const float u = acc[1][m][n][i];
-                    const float prod = (g * sigmoid_f32(g)) * u;
-                    static_cast<uint16_t*>(a.out)[orow * a.N + col] = f32_to_bf16_rne(prod);
-                } else {
-                    static_cast<float*>(a.out)[orow * a.N + col] = acc[0][m][n][i];
+                    s_h[r * HS + wn * WN_OUT + n * 32 + r32] = f32_to_bf16_rne(silu_f32(g) * u);
                 }
             }
+        }
+        __syncthreads();
+        constexpr int CPR = BN_OUT / 8;  // 16-byte chunks per row
+        uint16_t* out = static_cast<uint16_t*>(a.out);
+        for (int q = tid; q < rows * CPR; q += kThreads) {
+            const int r = q / CPR, c = (q % CPR) * 8;
+            *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(out_row0 + r) * a.N + n0 + c) =
+                *reinterpret_cast<const u32x4*>(&s_h[r * HS + c]);
+        }
+    } else {
+        // y tile: fp32, staged 128 rows at a time (row stride BN_OUT + 8
+        // floats puts rows 4 apart 32 banks apart)
+        constexpr int YS = BN_OUT + 8;
+        constexpr int HALF_ROWS = BM / 2;
+        static_assert(HALF_ROWS * YS * 4 <= ARENA * 2, "y half tile fits the arena");
+        static_assert(MB % 2 == 0, "row halves split each wave's blocks evenly");
+        float* s_y = reinterpret_cast<float*>(s_arena);
+        float* out = static_cast<float*>(a.out);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            // blocks wm + WAVES_M * m with m in [hh*MB/2, (hh+1)*MB/2) lie in
+            // rows [hh*HALF_ROWS, (hh+1)*HALF_ROWS)
+#pragma unroll
+            for (int m = hh * (MB / 2); m < (hh + 1) * (MB / 2); ++m) {
+                if (m >= mb_valid) continue;
+                const int blk = wm + WAVES_M * m;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3) - hh * HALF_ROWS;
+#pragma unroll
+                    for (int n = 0; n < NB; ++n)
+                        s_y[r * YS + wn * WN_OUT + n * 32 + r32] = acc[0][m][n][i];
+                }
+            }
+            __syncthreads();
+            constexpr int CPR = BN_OUT / 4;
+            const int hrows = min(HALF_ROWS, rows - hh * HALF_ROWS);
+            for (int q = tid; q < hrows * CPR; q += kThreads) {
+                const int r = q / CPR, c = (q % CPR) * 4;
+                *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(out_row0 + hh * HALF_ROWS + r) * a.N + n0 + c) =
+                    *reinterpret_cast<const u32x4*>(&s_y[r * YS + c]);
+            }
+            if (hh == 0) __syncthreads();
         }
     }
 }
@@ -576,6 +628,318 @@ hipError_t launch_gemm32(const FfnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Direct-to-LDS variant of the large-tile GEMM (the one the library uses for
+// experts with many rows).
+//
+// Same tile (256 x 256, 4 waves of 128 x 128, 32x32x16 MFMA) and tile map as
+// ffn_gemm32_kernel, but global data goes straight into LDS with
+// buffer_load_dwordx4 ... lds: no staging registers and no LDS store
+// instructions.  Each such load writes one wave's 64 x 16 bytes contiguously
+// at M0, so a tile stage (K = 64, 128 bytes per row) is laid out row-major
+// without padding, and the 16-byte chunk c of row r sits at chunk
+// c ^ ((r >> 1) & 7): the 16 rows read by one MFMA operand load then hit all
+// 64 banks once.  The 160 KB of LDS hold two activation stages and three
+// weight stages: activations (mostly L2 hits) are loaded one stage ahead,
+// weights (the HBM stream) two stages ahead.  The compiler does not see these
+// loads, so the kernel itself waits for them (vmcnt) before each barrier.
+constexpr int kDmaArena = 163840;  // the whole LDS of a gfx950 workgroup
+
+__device__ __forceinline__ void dma_load16(uint32_t lds_byte_addr, __amdgpu_buffer_rsrc_t rsrc,
+                                           uint32_t voffset, uint32_t soffset) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, %3 offen lds"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_byte_addr)), "v"(voffset), "s"(rsrc),
+          "s"(__builtin_amdgcn_readfirstlane(soffset))
+        : "memory", "m0");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+template <bool GATEUP>
+__global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
+    constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 2;
+    constexpr int BN_OUT = GATEUP ? BN / 2 : BN;
+    constexpr int MB = BM / 32 / WAVES_M;      // 4 row blocks per wave
+    constexpr int WN_OUT = BN_OUT / WAVES_N;
+    constexpr int NB = WN_OUT / 32;
+    constexpr int NACC = GATEUP ? 2 : 1;
+    constexpr int NFB = NACC * NB;             // B fragments per substep (4)
+    constexpr int ROW_BYTES = BK * 2;          // 128
+    constexpr int A_STAGE = BM * ROW_BYTES;    // 32 KB
+    constexpr int B_STAGE = BN * ROW_BYTES;    // 32 KB
+    constexpr int A_BUFS = 2, B_BUFS = 3;
+    static_assert(A_BUFS * A_STAGE + B_BUFS * B_STAGE == kDmaArena, "LDS budget");
+    constexpr int DMA_PER_WAVE = BM / kWaves / 8;  // 1-KB loads per wave per operand (8)
+
+    __shared__ __attribute__((aligned(1024))) unsigned char s_arena[kDmaArena];
+    const uint32_t arena = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_arena));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+
+    int e, nt, row0, rows;
+    {
+        int32_t* s_off = reinterpret_cast<int32_t*>(s_arena);
+        int32_t* s_tstart = s_off + (kMaxE + 1);
+        if (!find_tile<BM>(a, a.N / BN_OUT, s_off, s_tstart, e, nt, row0, rows)) return;
+        __syncthreads();  // everyone is done with the schedule before DMA reuses the arena
+    }
+    const int n0 = nt * BN_OUT;
+    const int K = a.K;
+    const int nblk = (rows + 31) >> 5;
+
+    // ---- DMA addressing: wave w fills rows [64 w, 64 w + 64) of a stage,
+    // 8 rows per load; lane L of load j writes row 64 w + 8 j + L / 8, physical
+    // chunk L % 8, i.e. logical chunk (L % 8) ^ ((row >> 1) & 7). ----
+    constexpr uint32_t kOutside = 0x80000000u;
+    __amdgpu_buffer_rsrc_t rsrc_a, rsrc_b;
+    uint32_t va[DMA_PER_WAVE], vb[DMA_PER_WAVE];
+    if constexpr (GATEUP)
+        rsrc_a = make_rsrc(a.a_src, static_cast<uint32_t>(a.T * K * 2));
+    else
+        rsrc_a = make_rsrc(a.a_src + static_cast<int64_t>(row0) * K,
+                           static_cast<uint32_t>(rows * K * 2));
+    {
+        const int64_t first = (static_cast<int64_t>(e) * a.N + n0) * K;
+        const uint16_t* wbase;
+        if constexpr (GATEUP)
+            wbase = (wave < 2 ? a.b0 : a.b1) + first;  // waves 0-1: gate rows, 2-3: up rows
+        else
+            wbase = a.b0 + first;
+        rsrc_b = make_rsrc(wbase, static_cast<uint32_t>((GATEUP ? BN_OUT : BN) * K * 2));
+    }
+#pragma unroll
+    for (int j = 0; j < DMA_PER_WAVE; ++j) {
+        const int r = wave * 64 + j * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        uint32_t av;
+        if (r >= nblk * 32) {
+            av = kOutside;
+        } else if constexpr (GATEUP) {
+            const int rr = min(r, rows - 1);
+            int64_t tok = a.sorted_pairs[row0 + rr] / a.k;
+            tok = tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
+            av = static_cast<uint32_t>(tok * K * 2 + c * 16);
+        } else {
+            av = static_cast<uint32_t>(r * K * 2 + c * 16);
+        }
+        va[j] = av;
+        const int rb = GATEUP ? (r & (BN_OUT - 1)) : r;  // row within the gate / up half
+        vb[j] = static_cast<uint32_t>(rb * K * 2 + c * 16);
+    }
+    auto a_buf = [&](int i) { return arena + i * A_STAGE; };
+    auto b_buf = [&](int i) { return arena + A_BUFS * A_STAGE + i * B_STAGE; };
+    auto dma_a = [&](int j, int buf, int kt) {
+        dma_load16(a_buf(buf) + (wave * 64 + j * 8) * ROW_BYTES, rsrc_a, va[j],
+                   static_cast<uint32_t>(kt * ROW_BYTES));
+    };
+    auto dma_b = [&](int j, int buf, int kt) {
+        dma_load16(b_buf(buf) + (wave * 64 + j * 8) * ROW_BYTES, rsrc_b, vb[j],
+                   static_cast<uint32_t>(kt * ROW_BYTES));
+    };
+
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int r32 = lane & 31, half = lane >> 5;
+    int mb_valid = 0;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) mb_valid += (wm + WAVES_M * mb) < nblk;
+
+    f32x16 acc[NACC][MB][NB];
+#pragma unroll
+    for (int g = 0; g < NACC; ++g)
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int n = 0; n < NB; ++n)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) acc[g][m][n][i] = 0.0f;
+
+    // LDS byte offset of the fragment (row r, logical chunk c) of a stage
+    auto frag_off = [&](int r, int c) { return r * ROW_BYTES + ((c ^ ((r >> 1) & 7)) << 4); };
+
+    auto k_loop = [&](auto nv_tag) {
+        constexpr int NV = decltype(nv_tag)::value;
+        constexpr int NA = NV > 0 ? NV : 1;
+        constexpr int MF = NV * NFB;  // MFMAs per substep
+        struct Frags {
+            bf16x8 a[NA];
+            bf16x8 b[NFB];
+        };
+        auto load_frags = [&](Frags& f, int abuf, int bbuf, int ks) {
+            const int c = ks * 2 + half;
+            const unsigned char* sa = s_arena + (a_buf(abuf) - arena);
+            const unsigned char* sb = s_arena + (b_buf(bbuf) - arena);
+#pragma unroll
+            for (int m = 0; m < NV; ++m)
+                f.a[m] = *reinterpret_cast<const bf16x8*>(
+                    sa + frag_off((wm + WAVES_M * m) * 32 + r32, c));
+            if constexpr (NV > 0) {
+#pragma unroll
+                for (int g = 0; g < NACC; ++g)
+#pragma unroll
+                    for (int n = 0; n < NB; ++n)
+                        f.b[g * NB + n] = *reinterpret_cast<const bf16x8*>(
+                            sb + frag_off(g * BN_OUT + wn * WN_OUT + n * 32 + r32, c));
+            }
+        };
+        auto mfma_one = [&](const Frags& f, auto ic) {
+            constexpr int i = decltype(ic)::value;      // i = (g * NB + n) * NV + m
+            constexpr int m = i % (NV > 0 ? NV : 1);
+            constexpr int gn = i / (NV > 0 ? NV : 1);
+            constexpr int g = gn / NB, n = gn % NB;
+            if constexpr (NV > 0) acc[g][m][n] = mfma32(f.a[m], f.b[gn], acc[g][m][n]);
+        };
+        auto mfmas = [&](const Frags& f) {
+            static_for<0, MF>([&](auto ic) { mfma_one(f, ic); });
+        };
+        const int nk = K / BK;
+        // prologue: A(0), B(0), B(1) in flight; wait for the first two
+#pragma unroll
+        for (int j = 0; j < DMA_PER_WAVE; ++j) dma_a(j, 0, 0);
+#pragma unroll
+        for (int j = 0; j < DMA_PER_WAVE; ++j) dma_b(j, 0, 0);
+#pragma unroll
+        for (int j = 0; j < DMA_PER_WAVE; ++j) dma_b(j, 1, nk > 1 ? 1 : 0);
+        wait_vmcnt<DMA_PER_WAVE>();
+        __syncthreads();
+        int abuf = 0, bbuf = 0;
+        for (int kt = 0; kt < nk; ++kt) {
+            const int ka = kt + 1 < nk ? kt + 1 : nk - 1;   // past the end: refill an idle buffer
+            const int kb = kt + 2 < nk ? kt + 2 : nk - 1;
+            const int anext = abuf ^ 1;
+            const int bnext = bbuf == 0 ? 2 : bbuf - 1;     // (bbuf + 2) % 3
+            // Phases are pinned with scheduling fences (the compiler would
+            // otherwise sink fragment reads next to their MFMAs): fragment
+            // reads of a substep are issued one substep ahead, and the
+            // stage's 16 loads are spread evenly over its MFMAs (activations
+            // first, they are needed one stage ahead; weights after), so the
+            // texture unit never backs up into the MFMA issue stream.
+            Frags f0, f1;
+            load_frags(f0, abuf, bbuf, 0);
+            load_frags(f1, abuf, bbuf, 1);
+            __builtin_amdgcn_sched_barrier(0);
+            constexpr int LPS = 2 * DMA_PER_WAVE / 4;  // loads per substep (4)
+            auto substep = [&](const Frags& f, auto sc) {
+                constexpr int sub = decltype(sc)::value;
+                static_for<0, (MF > LPS ? MF : LPS)>([&](auto ic) {
+                    constexpr int i = decltype(ic)::value;
+                    if constexpr (i < MF) mfma_one(f, ic);
+                    // one load after every (MF / LPS)-th MFMA
+                    constexpr int step = MF >= LPS ? MF / LPS : 1;
+                    if constexpr (i % step == step - 1 && i / step < LPS) {
+                        constexpr int j = sub * LPS + i / step;
+                        if constexpr (j < DMA_PER_WAVE)
+                            dma_a(j, anext, ka);
+                        else
+                            dma_b(j - DMA_PER_WAVE, bnext, kb);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                });
+            };
+            substep(f0, std::integral_constant<int, 0>{});
+            load_frags(f0, abuf, bbuf, 2);
+            __builtin_amdgcn_sched_barrier(0);
+            substep(f1, std::integral_constant<int, 1>{});
+            load_frags(f1, abuf, bbuf, 3);
+            __builtin_amdgcn_sched_barrier(0);
+            substep(f0, std::integral_constant<int, 2>{});
+            substep(f1, std::integral_constant<int, 3>{});
+            // A(kt+1) and B(kt+1) have landed once only B(kt+2) is outstanding
+            wait_vmcnt<DMA_PER_WAVE>();
+            __syncthreads();
+            abuf = anext;
+            bbuf = bbuf == 2 ? 0 : bbuf + 1;
+        }
+        wait_vmcnt<0>();
+        __syncthreads();
+    };
+    switch (mb_valid) {
+        case 0: k_loop(std::integral_constant<int, 0>{}); break;
+        case 1: k_loop(std::integral_constant<int, 1>{}); break;
+        case 2: k_loop(std::integral_constant<int, 2>{}); break;
+        case 3: k_loop(std::integral_constant<int, 3>{}); break;
+        default: k_loop(std::integral_constant<int, 4>{}); break;
+    }
+
+    // ---- epilogue: stage the output tile in LDS, then 16-byte stores ----
+    if constexpr (GATEUP) {
+        constexpr int HS = BN_OUT + 8;
+        uint16_t* s_h = reinterpret_cast<uint16_t*>(s_arena);
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            if (m >= mb_valid) continue;
+            const int blk = wm + WAVES_M * m;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const int r = blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+#pragma unroll
+                for (int n = 0; n < NB; ++n) {
+                    const float g = acc[0][m][n][i];
+                    const float u = acc[1][m][n][i];
+                    s_h[r * HS + wn * WN_OUT + n * 32 + r32] = f32_to_bf16_rne(silu_f32(g) * u);
+                }
+            }
+        }
+        __syncthreads();
+        constexpr int CPR = BN_OUT / 8;
+        uint16_t* out = static_cast<uint16_t*>(a.out);
+        for (int q = tid; q < rows * CPR; q += kThreads) {
+            const int r = q / CPR, c = (q % CPR) * 8;
+            *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(row0 + r) * a.N + n0 + c) =
+                *reinterpret_cast<const u32x4*>(&s_h[r * HS + c]);
+        }
+    } else {
+        constexpr int YS = BN_OUT + 8;
+        constexpr int HALF_ROWS = BM / 2;
+        static_assert(HALF_ROWS * YS * 4 <= kDmaArena, "y half tile fits");
+        float* s_y = reinterpret_cast<float*>(s_arena);
+        float* out = static_cast<float*>(a.out);
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+#pragma unroll
+            for (int m = hh * (MB / 2); m < (hh + 1) * (MB / 2); ++m) {
+                if (m >= mb_valid) continue;
+                const int blk = wm + WAVES_M * m;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const int r = blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3) - hh * HALF_ROWS;
+#pragma unroll
+                    for (int n = 0; n < NB; ++n) s_y[r * YS + wn * WN_OUT + n * 32 + r32] = acc[0][m][n][i];
+                }
+            }
+            __syncthreads();
+            constexpr int CPR = BN_OUT / 4;
+            const int hrows = min(HALF_ROWS, rows - hh * HALF_ROWS);
+            for (int q = tid; q < hrows * CPR; q += kThreads) {
+                const int r = q / CPR, c = (q % CPR) * 4;
+                *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(row0 + hh * HALF_ROWS + r) * a.N + n0 + c) =
+                    *reinterpret_cast<const u32x4*>(&s_y[r * YS + c]);
+            }
+            if (hh == 0) __syncthreads();
+        }
+    }
+}
+
+template <bool GATEUP>
+hipError_t launch_gemm_dma(const FfnArgs& a, hipStream_t s) {
+    constexpr int BM = 256, BN_OUT = GATEUP ? 128 : 256;
+    const int64_t mtiles = (a.P + BM - 1) / BM + (a.E < a.P ? a.E : a.P);
+    const int64_t tiles = mtiles * (a.N / BN_OUT);
+    const int64_t grid = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
+    if (grid <= 0) return hipSuccess;
+    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    ffn_gemm_dma_kernel<GATEUP><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s>>>(a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* sorted_pairs,
@@ -589,7 +953,7 @@ hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* so
     const bool x_fits = p.T * static_cast<int64_t>(p.H) * 2 < (static_cast<int64_t>(1) << 31);
     if (rows_per_expert <= 96 || p.I % 128 != 0 || !x_fits)
         return launch_gemm<64, 128, 1, 4, true>(a, s);
-    return launch_gemm32<256, 256, 2, 2, true>(a, s);
+    return launch_gemm_dma<true>(a, s);
 }
 
 hipError_t launch_down(const Problem& p, const uint16_t* h, const int32_t* offsets,
@@ -600,7 +964,7 @@ hipError_t launch_down(const Problem& p, const uint16_t* h, const int32_t* offse
     if (rows_per_expert <= 24) return launch_gemm<16, 64, 1, 4, false>(a, s);
     if (rows_per_expert <= 96 || p.H % 256 != 0 || p.I % 128 != 0)
         return launch_gemm<64, 128, 1, 4, false>(a, s);
-    return launch_gemm32<256, 256, 2, 2, false>(a, s);
+    return launch_gemm_dma<false>(a, s);
 }
 
 hipError_t launch_expert_ffn(const Problem& p, const uint16_t* x, const int32_t* sorted_pairs,
