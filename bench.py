@@ -166,9 +166,11 @@ def cpu_baseline(res, target_s):
 
     if "OMP_NUM_THREADS" not in os.environ:
         os.environ["OMP_NUM_THREADS"] = str(len(os.sched_getaffinity(0)))
-    threads = int(os.environ["OMP_NUM_THREADS"])
+    os.environ.setdefault("OMP_PROC_BIND", "close")
     import oracle
     from group_limited_routing_router_amd.inputs import bits
+
+    threads = oracle.num_threads()
 
     cfg, d = res["cfg"], res["inputs"]
     wr = bits(d["w_router"])
@@ -191,7 +193,9 @@ def cpu_baseline(res, target_s):
         t_ffn = time.perf_counter() - t1
         return t_route + t_ffn
 
-    n0 = 2
+    # calibrate on enough tokens to keep every thread busy (a handful of
+    # tokens gives too few pairs and overstates the per-token time)
+    n0 = max(16, threads // 4)
     t0 = run(n0)
     n = int(max(4, min(cfg.T, round(target_s / max(t0 / n0, 1e-6)))))
     t = run(n)
@@ -220,7 +224,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the secondary decode (T=128) measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
     args = ap.parse_args()
@@ -291,6 +295,7 @@ def main():
             "hbm_gbs": round(dl["bytes"] / (dec["ms"] * 1e-3) / 1e9, 1),
             "hbm_frac": round(dl["bytes"] / (dec["ms"] * 1e-3) / PEAK_HBM, 4),
             "kernels_ms": {k: round(v, 4) for k, v in dec["kernel_ms"].items()},
+            "roofline": roofline_for(dec, max(dec["kernel_ms"], key=dec["kernel_ms"].get)),
         }
         log("[bench] decode T=128: %.3f ms/step, %.1f%% of HBM peak" % (
             dec["ms"], 100 * out["decode"]["hbm_frac"]))

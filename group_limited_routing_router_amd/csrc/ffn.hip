@@ -285,323 +285,6 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     }
 }
 
-// Large-tile variant for experts with many rows (prefill and longer).
-//
-// 32x32x16 MFMA; a 256-thread workgroup owns a BM x BN tile and each of its 4
-// waves a (BM/WAVES_M) x (BN/WAVES_N) sub-tile, 256 fp32 accumulators per lane
-// at the 256x256 / 2x2 shape.  Row blocks of 32 go to the M-waves cyclically
-// (block b to wave b % WAVES_M) and blocks past the tile's last row are
-// skipped, so a partly filled tile costs MFMA time in proportion to its rows.
-// K advances 64 at a time through two LDS buffers.  Weight tiles (the HBM
-// stream) are loaded two stages ahead into two register sets, activation
-// tiles (mostly L2 hits) one stage ahead; K must be a multiple of 128.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
-__global__ __launch_bounds__(kThreads) void ffn_gemm32_kernel(FfnArgs a) {
-    static_assert(WAVES_M * WAVES_N == kWaves, "4 waves");
-    constexpr int BN_OUT = GATEUP ? BN / 2 : BN;
-    constexpr int MBLK = BM / 32;                    // row blocks per tile
-    constexpr int MB = MBLK / WAVES_M;               // row blocks per wave
-    constexpr int WN_OUT = BN_OUT / WAVES_N;
-    constexpr int NB = WN_OUT / 32;
-    constexpr int NACC = GATEUP ? 2 : 1;
-    static_assert(MB >= 1 && NB >= 1 && MBLK % WAVES_M == 0, "tile shape");
-    constexpr int A_ITERS = BM * (BK / 8) / kThreads;  // 16-byte chunks per thread
-    constexpr int B_ITERS = BN * (BK / 8) / kThreads;
-    static_assert(A_ITERS * kThreads == BM * (BK / 8) && B_ITERS * kThreads == BN * (BK / 8), "");
-    // chunk i of a thread covers tile row (tid / 8) + 32 * i: one 32-row block
-    static_assert(kThreads / 8 == 32, "loader row mapping");
-
-    // One LDS arena: two A and two B stage buffers during the K loop, then
-    // the output tile staged for wide stores in the epilogue.
-    constexpr int A_ELEMS = BM * LDS_STRIDE, B_ELEMS = BN * LDS_STRIDE;
-    constexpr int ARENA = 2 * (A_ELEMS + B_ELEMS);
-    __shared__ __attribute__((aligned(16))) uint16_t s_arena[ARENA];
-    uint16_t* const s_a[2] = {s_arena, s_arena + A_ELEMS};
-    uint16_t* const s_b[2] = {s_arena + 2 * A_ELEMS, s_arena + 2 * A_ELEMS + B_ELEMS};
-    __shared__ int32_t s_off[kMaxE + 1];
-    __shared__ int32_t s_tstart[kMaxE + 1];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-
-    int e, nt, row0, rows;
-    if (!find_tile<BM>(a, a.N / BN_OUT, s_off, s_tstart, e, nt, row0, rows)) return;
-    const int n0 = nt * BN_OUT;
-    const int K = a.K;
-    const int nblk = (rows + 31) >> 5;  // row blocks holding at least one row
-
-    // ---- loader addressing: buffer loads, 32-bit per-lane offsets ----
-    // Thread t loads 16-byte chunk (t % 8) of tile rows (t / 8) + 32 i; chunk
-    // i of a thread therefore lies in row block i.  Uniform parts of every
-    // offset (row block, K stage) go in the scalar offset.  Row blocks past
-    // the tile's rows get an offset outside the buffer, so their loads return
-    // zero without touching memory and the stage body has no branches.
-    const int lrow = tid >> 3, lcol = (tid & 7) * 8;
-    constexpr uint32_t kOutside = 0x80000000u;  // beyond every buffer used here
-    __amdgpu_buffer_rsrc_t rsrc_a, rsrc_b0, rsrc_b1;
-    uint32_t a_off[A_ITERS];
-    if constexpr (GATEUP) {
-        // rows of x gathered through sorted_pairs; x is [T, K]
-        rsrc_a = make_rsrc(a.a_src, static_cast<uint32_t>(a.T * K * 2));
-#pragma unroll
-        for (int i = 0; i < A_ITERS; ++i) {
-            const int r = min(lrow + 32 * i, rows - 1);
-            int64_t tok = a.sorted_pairs[row0 + r] / a.k;
-            tok = tok < 0 ? 0 : (tok >= a.T ? a.T - 1 : tok);
-            a_off[i] = i < nblk ? static_cast<uint32_t>((tok * K + lcol) * 2) : kOutside;
-        }
-    } else {
-        // rows of h are the tile's own rows, contiguous from row0
-        rsrc_a = make_rsrc(a.a_src + static_cast<int64_t>(row0) * K,
-                           static_cast<uint32_t>(rows * K * 2));
-#pragma unroll
-        for (int i = 0; i < A_ITERS; ++i)
-            a_off[i] = i < nblk ? static_cast<uint32_t>(((lrow + 32 * i) * K + lcol) * 2) : kOutside;
-    }
-    // weight rows of the tile: [n0, n0 + BN_OUT) of w_gate / w_up (gate/up) or
-    // of w_down (down), each K long
-    {
-        const int64_t first = (static_cast<int64_t>(e) * a.N + n0) * K;
-        rsrc_b0 = make_rsrc(a.b0 + first, static_cast<uint32_t>(BN_OUT * K * 2));
-        rsrc_b1 = GATEUP ? make_rsrc(a.b1 + first, static_cast<uint32_t>(BN_OUT * K * 2)) : rsrc_b0;
-    }
-    const uint32_t b_off = static_cast<uint32_t>((lrow * K + lcol) * 2);
-    const uint32_t b_soff_blk = static_cast<uint32_t>(32 * K * 2);
-
-    u32x4 ra[A_ITERS], ra2[A_ITERS], rb[B_ITERS], rb2[B_ITERS];
-    auto load_a = [&](u32x4 (&rax)[A_ITERS], int kt) {
-        const uint32_t kbytes = static_cast<uint32_t>(kt * BK * 2);
-#pragma unroll
-        for (int i = 0; i < A_ITERS; ++i)
-            rax[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, a_off[i], kbytes, 0);
-    };
-    auto load_b = [&](u32x4 (&rbx)[B_ITERS], int kt) {
-        const uint32_t kbytes = static_cast<uint32_t>(kt * BK * 2);
-        constexpr int HALF_ITERS = GATEUP ? B_ITERS / 2 : B_ITERS;
-#pragma unroll
-        for (int i = 0; i < B_ITERS; ++i)
-            rbx[i] = __builtin_amdgcn_raw_buffer_load_b128(i < HALF_ITERS ? rsrc_b0 : rsrc_b1, b_off,
-                                                           kbytes + (i % HALF_ITERS) * b_soff_blk, 0);
-    };
-    auto store_lds = [&](const u32x4 (&rax)[A_ITERS], const u32x4 (&rbx)[B_ITERS], int buf) {
-#pragma unroll
-        for (int i = 0; i < A_ITERS; ++i)
-            *reinterpret_cast<u32x4*>(&s_a[buf][(lrow + 32 * i) * LDS_STRIDE + lcol]) = rax[i];
-#pragma unroll
-        for (int i = 0; i < B_ITERS; ++i)
-            *reinterpret_cast<u32x4*>(&s_b[buf][(lrow + 32 * i) * LDS_STRIDE + lcol]) = rbx[i];
-    };
-
-    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
-    const int r32 = lane & 31, half = lane >> 5;
-    int mb_valid = 0;  // this wave's blocks wm, wm + WAVES_M, ... below nblk
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb) mb_valid += (wm + WAVES_M * mb) < nblk;
-
-    f32x16 acc[NACC][MB][NB];
-#pragma unroll
-    for (int g = 0; g < NACC; ++g)
-#pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-            for (int n = 0; n < NB; ++n)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) acc[g][m][n][i] = 0.0f;
-
-    // The K loop is compiled once per count NV of valid row blocks of this
-    // wave, so its MFMA sequence has no branches.  Within a stage the operand
-    // fragments of k-substep s+1 are read from LDS while the MFMAs of substep
-    // s run (two fragment register sets), the global loads of later stages are
-    // issued under the first substep, and the LDS stores of the next stage go
-    // under the last one.
-    auto k_loop = [&](auto nv_tag) {
-        constexpr int NV = decltype(nv_tag)::value;
-        constexpr int NA = NV > 0 ? NV : 1;
-        struct Frags {
-            bf16x8 a[NA];
-            bf16x8 b[NACC * NB];
-        };
-        auto load_frags = [&](Frags& f, int buf, int ks) {
-            const uint16_t* sa = s_a[buf];
-            const uint16_t* sb = s_b[buf];
-            const int kof = ks * 16 + half * 8;
-#pragma unroll
-            for (int m = 0; m < NV; ++m)
-                f.a[m] = *reinterpret_cast<const bf16x8*>(
-                    &sa[((wm + WAVES_M * m) * 32 + r32) * LDS_STRIDE + kof]);
-            if constexpr (NV > 0) {
-#pragma unroll
-                for (int g = 0; g < NACC; ++g)
-#pragma unroll
-                    for (int n = 0; n < NB; ++n)
-                        f.b[g * NB + n] = *reinterpret_cast<const bf16x8*>(
-                            &sb[(g * BN_OUT + wn * WN_OUT + n * 32 + r32) * LDS_STRIDE + kof]);
-            }
-        };
-        auto mfmas = [&](const Frags& f) {
-#pragma unroll
-            for (int g = 0; g < NACC; ++g)
-#pragma unroll
-                for (int n = 0; n < NB; ++n)
-#pragma unroll
-                    for (int m = 0; m < NV; ++m)
-                        acc[g][m][n] = mfma32(f.a[m], f.b[g * NB + n], acc[g][m][n]);
-        };
-        // one K stage from LDS buffer `buf`.
-        // Program order lists each group of work once; the scheduling-group
-        // fences at the end then spread the global loads, the fragment reads
-        // of the next substep and the LDS stores of the next stage between the
-        // MFMAs, so the MFMA unit is fed while the memory pipes work.
-        auto stage = [&](Frags& f0, Frags& f1, int buf, int kl, u32x4 (&ra_load)[A_ITERS],
-                         u32x4 (&rb_load)[B_ITERS], const u32x4 (&ra_store)[A_ITERS],
-                         const u32x4 (&rb_store)[B_ITERS]) {
-            load_frags(f0, buf, 0);
-            load_a(ra_load, kl);
-            load_b(rb_load, kl);
-            load_frags(f1, buf, 1);
-            mfmas(f0);
-            load_frags(f0, buf, 2);
-            mfmas(f1);
-            load_frags(f1, buf, 3);
-            mfmas(f0);
-            store_lds(ra_store, rb_store, buf ^ 1);
-            mfmas(f1);
-            if constexpr (NV > 0) {
-                constexpr int MF = NV * NACC * NB;          // MFMAs per substep
-                constexpr int FR = NV + NACC * NB;          // fragment reads per substep
-                constexpr int VM = A_ITERS + B_ITERS;       // global loads per stage
-                constexpr int WR = A_ITERS + B_ITERS;       // LDS stores per stage
-                constexpr int VM0 = (VM + 1) / 2;           // loads under substep 0
-                // fragments of substep 0 first (nothing to overlap them with)
-                __builtin_amdgcn_sched_group_barrier(0x100, FR, 0);
-                // substep 0: fragments of substep 1 and the first half of the loads
-                static_for<0, MF>([&](auto ic) {
-                    constexpr int i = decltype(ic)::value;
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if constexpr (i < FR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    if constexpr (i < VM0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                });
-                // substep 1: fragments of substep 2 and the rest of the loads
-                static_for<0, MF>([&](auto ic) {
-                    constexpr int i = decltype(ic)::value;
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if constexpr (i < FR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                    if constexpr (i < VM - VM0) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-                });
-                // substep 2: fragments of substep 3
-                static_for<0, MF>([&](auto ic) {
-                    constexpr int i = decltype(ic)::value;
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if constexpr (i < FR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-                });
-                // substep 3: the LDS stores of the next stage
-                static_for<0, MF>([&](auto ic) {
-                    constexpr int i = decltype(ic)::value;
-                    constexpr int n = (i + 1) * WR / MF - i * WR / MF;
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-                    if constexpr (n > 0) __builtin_amdgcn_sched_group_barrier(0x200, n, 0);
-                });
-            }
-            __syncthreads();
-        };
-        // nk is even (K % 128 == 0).  Global loads run two stages ahead in
-        // two register sets; the loop is unrolled by two so the sets never
-        // move.  Past the end, loads repeat the last stage and the store
-        // fills the buffer nobody reads.
-        const int nk = K / BK;
-        Frags f0, f1;
-        load_a(ra, 0);
-        load_b(rb, 0);
-        load_a(ra2, 1);
-        load_b(rb2, 1);
-        store_lds(ra, rb, 0);
-        __syncthreads();
-        for (int kt = 0; kt < nk; kt += 2) {
-            const int k2 = kt + 2 < nk ? kt + 2 : nk - 1;
-            const int k3 = kt + 3 < nk ? kt + 3 : nk - 1;
-            stage(f0, f1, 0, k2, ra, rb, ra2, rb2);
-            stage(f0, f1, 1, k3, ra2, rb2, ra, rb);
-        }
-    };
-    static_assert(MB <= 4, "k_loop dispatch covers up to 4 blocks per wave");
-    switch (mb_valid) {
-        case 0: k_loop(std::integral_constant<int, 0>{}); break;
-        case 1: k_loop(std::integral_constant<int, 1>{}); break;
-        case 2: k_loop(std::integral_constant<int, (MB >= 2 ? 2 : 1)>{}); break;
-        case 3: k_loop(std::integral_constant<int, (MB >= 3 ? 3 : 1)>{}); break;
-        default: k_loop(std::integral_constant<int, MB>{}); break;
-    }
-
-    // ---- epilogue: stage the output tile in LDS, then 16-byte stores ----
-    // (the K loop ended with a barrier, so the arena is free)
-    const int out_row0 = row0;
-    if constexpr (GATEUP) {
-        // h tile: rows x BN_OUT bf16, row stride BN_OUT + 8 (bank spread)
-        constexpr int HS = BN_OUT + 8;
-        static_assert(BM * HS <= ARENA, "h tile fits the arena");
-        uint16_t* s_h = s_arena;
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-            if (m >= mb_valid) continue;
-            const int blk = wm + WAVES_M * m;
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-#pragma unroll
-                for (int n = 0; n < NB; ++n) {
-                    const float g = acc[0][m][n][i];
-                    const float u = acc[1][m][n][i];
-                    s_h[r * HS + wn * WN_OUT + n * 32 + r32] = f32_to_bf16_rne(silu_f32(g) * u);
-                }
-            }
-        }
-        __syncthreads();
-        constexpr int CPR = BN_OUT / 8;  // 16-byte chunks per row
-        uint16_t* out = static_cast<uint16_t*>(a.out);
-        for (int q = tid; q < rows * CPR; q += kThreads) {
-            const int r = q / CPR, c = (q % CPR) * 8;
-            *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(out_row0 + r) * a.N + n0 + c) =
-                *reinterpret_cast<const u32x4*>(&s_h[r * HS + c]);
-        }
-    } else {
-        // y tile: fp32, staged 128 rows at a time (row stride BN_OUT + 8
-        // floats puts rows 4 apart 32 banks apart)
-        constexpr int YS = BN_OUT + 8;
-        constexpr int HALF_ROWS = BM / 2;
-        static_assert(HALF_ROWS * YS * 4 <= ARENA * 2, "y half tile fits the arena");
-        static_assert(MB % 2 == 0, "row halves split each wave's blocks evenly");
-        float* s_y = reinterpret_cast<float*>(s_arena);
-        float* out = static_cast<float*>(a.out);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            // blocks wm + WAVES_M * m with m in [hh*MB/2, (hh+1)*MB/2) lie in
-            // rows [hh*HALF_ROWS, (hh+1)*HALF_ROWS)
-#pragma unroll
-            for (int m = hh * (MB / 2); m < (hh + 1) * (MB / 2); ++m) {
-                if (m >= mb_valid) continue;
-                const int blk = wm + WAVES_M * m;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3) - hh * HALF_ROWS;
-#pragma unroll
-                    for (int n = 0; n < NB; ++n)
-                        s_y[r * YS + wn * WN_OUT + n * 32 + r32] = acc[0][m][n][i];
-                }
-            }
-            __syncthreads();
-            constexpr int CPR = BN_OUT / 4;
-            const int hrows = min(HALF_ROWS, rows - hh * HALF_ROWS);
-            for (int q = tid; q < hrows * CPR; q += kThreads) {
-                const int r = q / CPR, c = (q % CPR) * 4;
-                *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(out_row0 + hh * HALF_ROWS + r) * a.N + n0 + c) =
-                    *reinterpret_cast<const u32x4*>(&s_y[r * YS + c]);
-            }
-            if (hh == 0) __syncthreads();
-        }
-    }
-}
-
 template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
 hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
     constexpr int BN_OUT = GATEUP ? BN / 2 : BN;
@@ -615,33 +298,24 @@ hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
-hipError_t launch_gemm32(const FfnArgs& a, hipStream_t s) {
-    constexpr int BN_OUT = GATEUP ? BN / 2 : BN;
-    const int64_t mtiles = (a.P + BM - 1) / BM + (a.E < a.P ? a.E : a.P);
-    const int64_t tiles = mtiles * (a.N / BN_OUT);
-    const int64_t grid = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
-    if (grid <= 0) return hipSuccess;
-    if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    ffn_gemm32_kernel<BM, BN, WAVES_M, WAVES_N, GATEUP>
-        <<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s>>>(a);
-    return hipGetLastError();
-}
-
-// Direct-to-LDS variant of the large-tile GEMM (the one the library uses for
-// experts with many rows).
+// Large-tile GEMM for experts with many rows (prefill and longer).
 //
-// Same tile (256 x 256, 4 waves of 128 x 128, 32x32x16 MFMA) and tile map as
-// ffn_gemm32_kernel, but global data goes straight into LDS with
-// buffer_load_dwordx4 ... lds: no staging registers and no LDS store
-// instructions.  Each such load writes one wave's 64 x 16 bytes contiguously
-// at M0, so a tile stage (K = 64, 128 bytes per row) is laid out row-major
-// without padding, and the 16-byte chunk c of row r sits at chunk
-// c ^ ((r >> 1) & 7): the 16 rows read by one MFMA operand load then hit all
-// 64 banks once.  The 160 KB of LDS hold two activation stages and three
-// weight stages: activations (mostly L2 hits) are loaded one stage ahead,
-// weights (the HBM stream) two stages ahead.  The compiler does not see these
-// loads, so the kernel itself waits for them (vmcnt) before each barrier.
+// 32x32x16 MFMA; a 256-thread workgroup owns a 256 x 256 tile and each of its
+// 4 waves a 128 x 128 sub-tile, 256 fp32 accumulators per lane.  Row blocks
+// of 32 go to the two M-waves cyclically (block b to wave b % 2) and blocks
+// past the tile's last row are skipped, so a partly filled tile costs MFMA
+// time in proportion to its rows.  The tile map is find_tile's.
+//
+// Global data goes straight into LDS with buffer_load_dwordx4 ... lds: no
+// staging registers and no LDS store instructions.  Each such load writes one
+// wave's 64 x 16 bytes contiguously at M0, so a tile stage (K = 64, 128 bytes
+// per row) is laid out row-major without padding, and the 16-byte chunk c of
+// row r sits at chunk c ^ ((r >> 1) & 7): the 16 rows read by one MFMA
+// operand load then hit all 64 banks once.  The 160 KB of LDS hold two
+// activation stages and three weight stages: activations (mostly L2 hits)
+// are loaded one stage ahead, weights (the HBM stream) two stages ahead.  The
+// compiler does not see these loads, so the kernel itself waits for them
+// (vmcnt) before each barrier.
 constexpr int kDmaArena = 163840;  // the whole LDS of a gfx950 workgroup
 
 __device__ __forceinline__ void dma_load16(uint32_t lds_byte_addr, __amdgpu_buffer_rsrc_t rsrc,

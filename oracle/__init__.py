@@ -74,6 +74,8 @@ def _load():
         lib.oracle_combine.restype = ctypes.c_int
         lib.oracle_f32_to_bf16_rne.argtypes = [i64, P, P]
         lib.oracle_f32_to_bf16_rne.restype = None
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -200,6 +202,11 @@ def f32_to_bf16(a):
     out = np.empty(a.shape, np.uint16)
     lib.oracle_f32_to_bf16_rne(a.size, _ptr(a), _ptr(out))
     return out
+
+
+def num_threads():
+    """Threads the oracle's OpenMP loops run on."""
+    return int(_load().oracle_num_threads())
 
 
 def bf16_to_f32(bits):

@@ -31,6 +31,9 @@
  * any sum.
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -286,4 +289,13 @@ int oracle_combine(int64_t T, int32_t k, int32_t H, const float* y, const float*
 /* Exposed for tests that pin the rounding helper against a library cast. */
 void oracle_f32_to_bf16_rne(int64_t n, const float* src, uint16_t* dst) {
     for (int64_t i = 0; i < n; ++i) dst[i] = float_to_bf16_bits_rne(src[i]);
+}
+
+/* Number of threads the parallel loops above use (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
 }
