@@ -8,120 +8,173 @@
 // router runs in FP32 (same page, section "Residual Stream").  Ties go to the
 // lower index.
 //
-// One workgroup of 8 waves owns 16*MB tokens and all E <= 256 experts.  The
+// One workgroup owns up to 16*MB tokens and all E <= 256 experts.  The
 // logits x . w_router^T are a small dense contraction with bf16 inputs and
-// fp32 accumulation, so they run on 16x16x32 bf16 MFMA: wave w covers the
-// expert quarter (w % 4) over half (w / 4) of the hidden dimension, and the
-// two halves meet in LDS.  Scores never leave LDS: group ranking and the
-// top-k run in the same kernel, one wave per token, with the k picks done as
-// k wave-wide arg-max reductions.
+// fp32 accumulation, so they run on 16x16x32 bf16 MFMA.  The hidden dimension
+// is walked 64 at a time: the workgroup loads the router-weight tile (256
+// experts x 128 bytes) and the token tile with coalesced 16-byte loads, a
+// few steps ahead into registers, writes the current step to LDS and every
+// wave reads its MFMA operands from there (loading MFMA operands straight
+// from memory would give every lane of a quad its own row and cache access).
+// Each wave owns a set of 16-expert blocks and accumulates its logits over
+// the steps in order.  Scores never leave LDS: group ranking and the top-k
+// run in the same kernel, one wave per token, with the k picks done as k
+// wave-wide arg-max reductions.
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int kRouteThreads = 512;
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 16;
+constexpr int kRowBytes = 128;          // one 64-wide step of a bf16 row
+constexpr int kWTile = kMaxE * kRowBytes;  // router-weight tile of one step (32 KB)
 
-template <int MB>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(
-    int64_t T, int H, int E, int G, int TG, int k, const uint16_t* __restrict__ x,
+// LDS byte offset of 16-byte chunk c of row r in a staged tile: chunks are
+// XOR-swizzled so the 16 rows of one MFMA operand read hit distinct banks.
+__device__ __forceinline__ int stage_off(int r, int c) {
+    return r * kRowBytes + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+// NW waves; a workgroup owns tpw <= TT = 16 * MB tokens (with few tokens a
+// workgroup takes fewer than 16 so that more compute units share the work;
+// MFMA rows past tpw repeat a valid row and are dropped).  D: steps loaded
+// ahead into registers.
+template <int MB, int NW, int D>
+__global__ __launch_bounds__(64 * NW) void route_kernel(
+    int64_t T, int H, int E, int G, int TG, int k, int tpw, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ wr, const float* __restrict__ bias, int32_t* __restrict__ ids,
     float* __restrict__ weights) {
+    constexpr int NT = 64 * NW;
     constexpr int TT = 16 * MB;
+    constexpr int BPW = kMaxE / 16 / NW;          // 16-expert blocks per wave
+    constexpr int XTILE = TT * kRowBytes;
+    constexpr int STAGE = kWTile + XTILE;
+    constexpr int WL = kWTile / 16 / NT;          // weight loads per thread and step
+    constexpr int XL = (TT * 8 + NT - 1) / NT;    // token loads per thread and step
+    static_assert(WL * 16 * NT == kWTile, "whole weight tile per step");
+    struct Gather {                               // the loads of one step (ring of D)
+        u32x4 w[WL];
+        u32x4 x[XL];
+    };
+    __shared__ __attribute__((aligned(16))) unsigned char s_stage[2][STAGE];
     __shared__ float s_score[TT][kMaxE + 4];
-    __shared__ float s_gscore[TT][kMaxE];      // group score (G <= E <= 256)
-    __shared__ unsigned char s_kept[TT][kMaxE];
+    // group scores and kept flags reuse the staging area once the logits are done
+    static_assert(TT * kMaxE * 4 + TT * kMaxE <= 2 * STAGE, "selection scratch fits");
+    float (*s_gscore)[kMaxE] = reinterpret_cast<float (*)[kMaxE]>(&s_stage[0][0]);
+    unsigned char (*s_kept)[kMaxE] =
+        reinterpret_cast<unsigned char (*)[kMaxE]>(&s_stage[0][0] + TT * kMaxE * 4);
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int eq = wave & 3;      // expert quarter
-    const int kh = wave >> 2;     // hidden half
-    const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * TT;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave
+    const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * tpw;
 
-    // ---- logits: D[token][expert] over this wave's hidden half ----
-    const int nblk = (E + 15) >> 4;  // 16-expert blocks
-    f32x4 acc[4][MB];
+    // ---- coalesced load addressing: eight threads per 128-byte row ----
+    const uint16_t* wsrc[WL];
+    int wdst[WL];
 #pragma unroll
-    for (int b = 0; b < 4; ++b)
+    for (int j = 0; j < WL; ++j) {
+        const int q = j * NT + tid;
+        const int r = q >> 3, c = q & 7;
+        const int e = r < E ? r : E - 1;  // rows past the last expert repeat it; dropped
+        wsrc[j] = wr + static_cast<int64_t>(e) * H + c * 8;
+        wdst[j] = stage_off(r, c);
+    }
+    const uint16_t* xsrc[XL];
+    int xdst[XL];
+#pragma unroll
+    for (int j = 0; j < XL; ++j) {
+        const int q = j * NT + tid;
+        const int r = (q >> 3) < TT ? (q >> 3) : TT - 1;
+        const int c = q & 7;
+        int64_t t = tok0 + (r < tpw ? r : tpw - 1);
+        if (t > T - 1) t = T - 1;  // padded rows read a valid row; results dropped
+        xsrc[j] = x + t * H + c * 8;
+        xdst[j] = (q >> 3) < TT ? kWTile + stage_off(r, c) : -1;
+    }
+    const int nsteps = H >> 6;
+    auto gather = [&](Gather& g, int st) {
+        const int off = (st < nsteps ? st : nsteps - 1) * 64;  // past the end: repeat
+#pragma unroll
+        for (int j = 0; j < WL; ++j) g.w[j] = ld16(wsrc[j] + off);
+#pragma unroll
+        for (int j = 0; j < XL; ++j) g.x[j] = ld16(xsrc[j] + off);
+    };
+    auto put = [&](const Gather& g, int buf) {
+        unsigned char* base = &s_stage[buf][0];
+#pragma unroll
+        for (int j = 0; j < WL; ++j) *reinterpret_cast<u32x4*>(base + wdst[j]) = g.w[j];
+#pragma unroll
+        for (int j = 0; j < XL; ++j)
+            if (xdst[j] >= 0) *reinterpret_cast<u32x4*>(base + xdst[j]) = g.x[j];
+    };
+
+    // ---- logits: this wave's expert blocks wave, wave + NW, ... ----
+    f32x4 acc[BPW][MB];
+#pragma unroll
+    for (int b = 0; b < BPW; ++b)
 #pragma unroll
         for (int m = 0; m < MB; ++m) acc[b][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
     const int r16 = lane & 15;
-    const int q = lane >> 4;  // which 16-element k chunk of a 64-wide step
-    const uint16_t* xrow[MB];
+    const int q = lane >> 4;  // which 8-element k chunk of a 32-wide MFMA step
+    auto compute = [&](int buf) {
+        const unsigned char* base = &s_stage[buf][0];
 #pragma unroll
-    for (int m = 0; m < MB; ++m) {
-        int64_t t = tok0 + m * 16 + r16;
-        if (t > T - 1) t = T - 1;  // padded rows read a valid row; results dropped
-        xrow[m] = x + t * H;
-    }
-    const uint16_t* wrow[4];
+        for (int h = 0; h < 2; ++h) {  // two 32-wide MFMA steps per 64-wide step
+            const int c = h * 4 + q;
+            bf16x8 a[MB], b[BPW];
 #pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        int e = (eq + 4 * b) * 16 + r16;
-        if (e > E - 1) e = E - 1;
-        wrow[b] = wr + static_cast<int64_t>(e) * H;
-    }
-    const int half = H >> 1;
-    const int k0 = kh * half;
-    for (int kk = k0; kk < k0 + half; kk += 64) {
-        const int off = kk + q * 16;
-        bf16x8 a0[MB], a1[MB];
+            for (int m = 0; m < MB; ++m)
+                a[m] = *reinterpret_cast<const bf16x8*>(base + kWTile + stage_off(m * 16 + r16, c));
 #pragma unroll
-        for (int m = 0; m < MB; ++m) {
-            a0[m] = as_bf16x8(ld16(xrow[m] + off));
-            a1[m] = as_bf16x8(ld16(xrow[m] + off + 8));
+            for (int bb = 0; bb < BPW; ++bb)
+                b[bb] = *reinterpret_cast<const bf16x8*>(
+                    base + stage_off((wave + NW * bb) * 16 + r16, c));
+#pragma unroll
+            for (int bb = 0; bb < BPW; ++bb)
+#pragma unroll
+                for (int m = 0; m < MB; ++m) acc[bb][m] = mfma16(a[m], b[bb], acc[bb][m]);
         }
+    };
+    {
+        Gather ring[D];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            if (eq + 4 * b >= nblk) break;
-            bf16x8 b0 = as_bf16x8(ld16(wrow[b] + off));
-            bf16x8 b1 = as_bf16x8(ld16(wrow[b] + off + 8));
+        for (int d = 0; d < D; ++d) gather(ring[d], d);
+        // step st: stage the loads of step st, refill their registers with step
+        // st + D, then run the step's MFMAs; two LDS buffers alternate
+        for (int st0 = 0; st0 < nsteps; st0 += D) {
 #pragma unroll
-            for (int m = 0; m < MB; ++m) {
-                acc[b][m] = mfma16(a0[m], b0, acc[b][m]);
-                acc[b][m] = mfma16(a1[m], b1, acc[b][m]);
+            for (int d = 0; d < D; ++d) {
+                const int st = st0 + d;
+                if (st < nsteps) {  // uniform
+                    put(ring[d], st & 1);
+                    __syncthreads();
+                    gather(ring[d], st + D);
+                    compute(st & 1);
+                }
             }
         }
     }
+    __syncthreads();  // staging buffers are reused below
 
-    // ---- meet the two halves in LDS, add bias, sigmoid ----
-    if (kh == 1) {
+    // ---- bias and sigmoid into s_score ----
 #pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int e = (eq + 4 * b) * 16 + r16;
-            if (eq + 4 * b >= nblk || e >= E) continue;
+    for (int bb = 0; bb < BPW; ++bb) {
+        const int e = (wave + NW * bb) * 16 + r16;
+        if (e >= E) continue;
+        const float be = bias ? bias[e] : 0.0f;
 #pragma unroll
-            for (int m = 0; m < MB; ++m)
+        for (int m = 0; m < MB; ++m)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) s_score[m * 16 + q * 4 + i][e] = acc[b][m][i];
-        }
-    }
-    __syncthreads();
-    if (kh == 0) {
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-            const int e = (eq + 4 * b) * 16 + r16;
-            if (eq + 4 * b >= nblk || e >= E) continue;
-            const float be = bias ? bias[e] : 0.0f;
-#pragma unroll
-            for (int m = 0; m < MB; ++m)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float& s = s_score[m * 16 + q * 4 + i][e];
-                    s = sigmoid_f32((acc[b][m][i] + s) + be);
-                }
-        }
+            for (int i = 0; i < 4; ++i) s_score[m * 16 + q * 4 + i][e] = sigmoid_f32(acc[bb][m][i] + be);
     }
     __syncthreads();
 
     // ---- group scores: sum of each group's two best scores ----
     const int gs = E / G;
-    for (int item = tid; item < TT * G; item += kRouteThreads) {
+    for (int item = tid; item < TT * G; item += NT) {
         const int tt = item / G, g = item - tt * G;
         const float* s = &s_score[tt][g * gs];
         float t1 = s[0], t2 = -1.0f;
@@ -138,7 +191,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
     __syncthreads();
     // ---- kept groups: rank under (score desc, index asc) below TG ----
-    for (int item = tid; item < TT * G; item += kRouteThreads) {
+    for (int item = tid; item < TT * G; item += NT) {
         const int tt = item / G, g = item - tt * G;
         const float mine = s_gscore[tt][g];
         int rank = 0;
@@ -151,7 +204,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     __syncthreads();
 
     // ---- top-k among kept groups: one wave per token ----
-    for (int tt = wave; tt < TT; tt += kRouteThreads / kWave) {
+    for (int tt = wave; tt < tpw; tt += NT / kWave) {
         const int64_t t = tok0 + tt;
         if (t >= T) break;  // wave-uniform; no barrier follows
         float v[4];
@@ -210,13 +263,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 hipError_t launch_route(const Problem& p, const uint16_t* x, const uint16_t* w_router,
                         const float* bias, int32_t* ids, float* weights, hipStream_t s) {
     if (p.T >= 4096) {
+        // many tokens: 32-token tiles (the router weight is read once per tile)
         const int64_t grid = (p.T + 31) / 32;
-        route_kernel<2><<<dim3(static_cast<unsigned>(grid)), dim3(kRouteThreads), 0, s>>>(
-            p.T, p.H, p.E, p.G, p.TG, p.k, x, w_router, bias, ids, weights);
+        route_kernel<2, 8, 3><<<dim3(static_cast<unsigned>(grid)), dim3(512), 0, s>>>(
+            p.T, p.H, p.E, p.G, p.TG, p.k, 32, x, w_router, bias, ids, weights);
     } else {
-        const int64_t grid = (p.T + 15) / 16;
-        route_kernel<1><<<dim3(static_cast<unsigned>(grid)), dim3(kRouteThreads), 0, s>>>(
-            p.T, p.H, p.E, p.G, p.TG, p.k, x, w_router, bias, ids, weights);
+        // few tokens: a workgroup takes only as many tokens (a power of two up
+        // to 16) as spread the batch over about 256 compute units
+        int tpw = 1;
+        while (tpw < 16 && (p.T + tpw - 1) / tpw > 256) tpw *= 2;
+        const int64_t grid = (p.T + tpw - 1) / tpw;
+        route_kernel<1, 16, 4><<<dim3(static_cast<unsigned>(grid)), dim3(1024), 0, s>>>(
+            p.T, p.H, p.E, p.G, p.TG, p.k, tpw, x, w_router, bias, ids, weights);
     }
     return hipGetLastError();
 }
