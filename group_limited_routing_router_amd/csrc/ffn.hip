@@ -315,7 +315,8 @@ hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
 // activation stages and three weight stages: activations (mostly L2 hits)
 // are loaded one stage ahead, weights (the HBM stream) two stages ahead.  The
 // compiler does not see these loads, so the kernel itself waits for them
-// (vmcnt) before each barrier.
+// (vmcnt) before each barrier, and for all of them before it ends.  Results
+// are stored straight from the accumulators (see the epilogue).
 constexpr int kDmaArena = 163840;  // the whole LDS of a gfx950 workgroup
 
 __device__ __forceinline__ void dma_load16(uint32_t lds_byte_addr, __amdgpu_buffer_rsrc_t rsrc,
@@ -334,6 +335,30 @@ template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Lanes of a quad exchange values so that a 4 x 4 block held one column per
+// lane (v[r] = row r) ends up one row per lane (v[c] = column c): two
+// butterfly stages, each one quad permute (DPP) and selects per value pair.
+__device__ __forceinline__ float dpp_xor1(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float dpp_xor2(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
+}
+__device__ __forceinline__ void quad_transpose(float& v0, float& v1, float& v2, float& v3) {
+    const int t = threadIdx.x & 3;
+    const bool b1 = (t & 2) != 0, b0 = (t & 1) != 0;
+    float y = dpp_xor2(b1 ? v0 : v2);  // rows 0/2 across lane bit 1
+    float n0 = b1 ? y : v0, n2 = b1 ? v2 : y;
+    y = dpp_xor2(b1 ? v1 : v3);
+    float n1 = b1 ? y : v1, n3 = b1 ? v3 : y;
+    y = dpp_xor1(b0 ? n0 : n1);        // rows 0/1 and 2/3 across lane bit 0
+    v0 = b0 ? y : n0;
+    v1 = b0 ? n1 : y;
+    y = dpp_xor1(b0 ? n2 : n3);
+    v2 = b0 ? y : n2;
+    v3 = b0 ? n3 : y;
 }
 
 template <bool GATEUP>
@@ -543,61 +568,45 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
         default: k_loop(std::integral_constant<int, 4>{}); break;
     }
 
-    // ---- epilogue: stage the output tile in LDS, then 16-byte stores ----
-    if constexpr (GATEUP) {
-        constexpr int HS = BN_OUT + 8;
-        uint16_t* s_h = reinterpret_cast<uint16_t*>(s_arena);
+    // ---- epilogue ----
+    {
+        // Straight from the accumulators: a quad transpose turns each lane's
+        // column of four rows into one row of four columns, so a lane stores 4
+        // contiguous outputs and one store instruction covers 8 rows x 32
+        // columns.
+        const int t = lane & 3, q4 = (lane & 31) >> 2;
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
             if (m >= mb_valid) continue;
             const int blk = wm + WAVES_M * m;
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int r = blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            for (int n = 0; n < NB; ++n) {
+                const int col = n0 + wn * WN_OUT + n * 32 + 4 * q4;
 #pragma unroll
-                for (int n = 0; n < NB; ++n) {
-                    const float g = acc[0][m][n][i];
-                    const float u = acc[1][m][n][i];
-                    s_h[r * HS + wn * WN_OUT + n * 32 + r32] = f32_to_bf16_rne(silu_f32(g) * u);
+                for (int j = 0; j < 4; ++j) {
+                    float v[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if constexpr (GATEUP)
+                            v[r] = silu_f32(acc[0][m][n][4 * j + r]) * acc[1][m][n][4 * j + r];
+                        else
+                            v[r] = acc[0][m][n][4 * j + r];
+                    }
+                    quad_transpose(v[0], v[1], v[2], v[3]);
+                    const int r = blk * 32 + 8 * j + 4 * half + t;
+                    if (r < rows) {
+                        const int64_t o = static_cast<int64_t>(row0 + r) * a.N + col;
+                        if constexpr (GATEUP) {
+                            const uint32_t lo = f32_to_bf16_rne(v[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
+                            const uint32_t hi = f32_to_bf16_rne(v[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
+                            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = u32x2{lo, hi};
+                        } else {
+                            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{v[0], v[1], v[2], v[3]};
+                        }
+                    }
                 }
             }
-        }
-        __syncthreads();
-        constexpr int CPR = BN_OUT / 8;
-        uint16_t* out = static_cast<uint16_t*>(a.out);
-        for (int q = tid; q < rows * CPR; q += kThreads) {
-            const int r = q / CPR, c = (q % CPR) * 8;
-            *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(row0 + r) * a.N + n0 + c) =
-                *reinterpret_cast<const u32x4*>(&s_h[r * HS + c]);
-        }
-    } else {
-        constexpr int YS = BN_OUT + 8;
-        constexpr int HALF_ROWS = BM / 2;
-        static_assert(HALF_ROWS * YS * 4 <= kDmaArena, "y half tile fits");
-        float* s_y = reinterpret_cast<float*>(s_arena);
-        float* out = static_cast<float*>(a.out);
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-            for (int m = hh * (MB / 2); m < (hh + 1) * (MB / 2); ++m) {
-                if (m >= mb_valid) continue;
-                const int blk = wm + WAVES_M * m;
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int r = blk * 32 + 8 * (i >> 2) + 4 * half + (i & 3) - hh * HALF_ROWS;
-#pragma unroll
-                    for (int n = 0; n < NB; ++n) s_y[r * YS + wn * WN_OUT + n * 32 + r32] = acc[0][m][n][i];
-                }
-            }
-            __syncthreads();
-            constexpr int CPR = BN_OUT / 4;
-            const int hrows = min(HALF_ROWS, rows - hh * HALF_ROWS);
-            for (int q = tid; q < hrows * CPR; q += kThreads) {
-                const int r = q / CPR, c = (q % CPR) * 4;
-                *reinterpret_cast<u32x4*>(out + static_cast<int64_t>(row0 + hh * HALF_ROWS + r) * a.N + n0 + c) =
-                    *reinterpret_cast<const u32x4*>(&s_y[r * YS + c]);
-            }
-            if (hh == 0) __syncthreads();
         }
     }
 }
