@@ -20,7 +20,10 @@ reduce to ``numpy.argsort`` / ``argmax``; the scores by a float64 library
 matmul; the permutation by ``numpy.bincount`` and a stable ``argsort``; the
 SwiGLU expert by ``torch.nn.functional`` on the CPU; the combine by the k=1
 and identical-experts closed forms; the whole block by the dense all-experts
-sum when k=E and G=1.  No function here is parity-unpinned.
+sum when k=E and G=1; the sublayer epilogue (``residual_norm``) by
+``torch.nn.functional.rms_norm`` at step 1 and by the closed forms of the
+stream update (scale of the stream, zero stream, orthogonal inputs).  No
+function here is parity-unpinned.
 """
 from __future__ import annotations
 
@@ -72,6 +75,8 @@ def _load():
         lib.oracle_ffn_pairs.restype = ctypes.c_int
         lib.oracle_combine.argtypes = [i64, i32, i32, P, P, f32, P]
         lib.oracle_combine.restype = ctypes.c_int
+        lib.oracle_residual_norm.argtypes = [i64, i32, P, P, f32, i32, P]
+        lib.oracle_residual_norm.restype = ctypes.c_int
         lib.oracle_f32_to_bf16_rne.argtypes = [i64, P, P]
         lib.oracle_f32_to_bf16_rne.restype = None
         lib.oracle_num_threads.argtypes = []
@@ -175,6 +180,21 @@ def combine(y, weights, scale):
     out = np.empty((T, H), np.float32)
     _check(lib.oracle_combine(T, k, H, _ptr(y), _ptr(w), float(scale), _ptr(out)), "combine")
     return out
+
+
+def residual_norm(o, gain, eps, step, residual):
+    """Post-norm of the sublayer output o [T,H] (RMSNorm with gain [H]) and the
+    residual-stream update at step `step`; returns the new stream [T,H]."""
+    lib = _load()
+    o = _c(o, np.float32)
+    T, H = o.shape
+    g = _c(gain, np.float32)
+    assert g.shape == (H,)
+    res = np.array(residual, dtype=np.float32, order="C", copy=True)
+    assert res.shape == (T, H)
+    _check(lib.oracle_residual_norm(T, H, _ptr(o), _ptr(g), float(eps), int(step), _ptr(res)),
+           "residual_norm")
+    return res
 
 
 def forward_with_routing(x, ids, weights, w_gate, w_up, w_down, scale, want_h=False):

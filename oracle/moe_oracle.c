@@ -286,6 +286,36 @@ int oracle_combine(int64_t T, int32_t k, int32_t H, const float* y, const float*
     return ORACLE_OK;
 }
 
+/* ---- sublayer epilogue: post-norm and the residual-stream update ----------
+ * "Welcome Beam: a 501B open model you can own, customize, and scale", section
+ * "Residual Stream": every sublayer output is normalised after the sublayer;
+ * the embedding is step 1 of the stream and step s adds the (normalised)
+ * sublayer output with weight 1/sqrt(s) while the stream keeps weight
+ * sqrt((s-1)/s); the norms compute in FP32.  Readings: the norm is RMSNorm
+ * (the only norm the page names) with a per-channel gain g and an eps added
+ * to the mean square; s = 1 replaces the stream by the normalised output.
+ *   n[m]   = (o[m] / sqrt(mean_m(o^2) + eps)) * g[m]
+ *   res[m] = sqrt((s-1)/s) * res[m] + (1/sqrt(s)) * n[m]
+ * All in fp32; the sum of squares runs in index order. */
+int oracle_residual_norm(int64_t T, int32_t H, const float* o, const float* g, float eps,
+                         int32_t step, float* res) {
+    if (T < 0 || H <= 0 || step < 1 || !(eps > 0.0f)) return ORACLE_ERR_ARG;
+    const float a = sqrtf((float)(step - 1) / (float)step);
+    const float b = 1.0f / sqrtf((float)step);
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const float* ot = o + t * H;
+        float ss = 0.0f;
+        for (int32_t m = 0; m < H; ++m) ss = ss + ot[m] * ot[m];
+        const float inv = 1.0f / sqrtf(ss / (float)H + eps);
+        for (int32_t m = 0; m < H; ++m) {
+            const float n = (ot[m] * inv) * g[m];
+            res[t * H + m] = a * res[t * H + m] + b * n;
+        }
+    }
+    return ORACLE_OK;
+}
+
 /* Exposed for tests that pin the rounding helper against a library cast. */
 void oracle_f32_to_bf16_rne(int64_t n, const float* src, uint16_t* dst) {
     for (int64_t i = 0; i < n; ++i) dst[i] = float_to_bf16_bits_rne(src[i]);
