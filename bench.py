@@ -61,6 +61,10 @@ def work_counts(cfg, n_hit):
         "gate_up": dict(flops=4 * P * H * I, bytes=n_hit * 2 * I * H * 2 + T * H * 2 + P * I * 2),
         "down": dict(flops=2 * P * I * H, bytes=n_hit * I * H * 2 + P * I * 2 + P * H * 4),
         "combine": dict(flops=2 * P * H, bytes=P * H * 4 + P * 8 + T * H * 4),
+        # combine fused with the post-norm and residual update: the stream is
+        # read and written, the combined output never leaves the chip
+        "combine_residual": dict(flops=2 * P * H + 6 * T * H,
+                                 bytes=P * H * 4 + P * 8 + 2 * T * H * 4 + H * 4),
     }
     layer = dict(flops=2 * T * H * E + 6 * P * H * I,
                  bytes=n_hit * w_expert + E * H * 2 + T * H * 2 + T * H * 4)
@@ -101,9 +105,11 @@ def run_workload(name, steps, warmup, weights, want_kernels=True):
     if want_kernels:
         # the same steps as separate calls, each bracketed by events on the
         # current stream (the stream the library launches on)
-        names = ["route", "permute", "gate_up", "down", "combine"]
+        names = ["route", "permute", "gate_up", "down", "combine", "combine_residual"]
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
               for _ in range(steps)]
+        gain = torch.ones(cfg.H, dtype=torch.float32, device="cuda")
+        stream_res = torch.zeros((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
         for it in range(warmup + steps):
             e = ev[it - warmup] if it >= warmup else None
             if e: e[0].record()
@@ -119,12 +125,54 @@ def run_workload(name, steps, warmup, weights, want_kernels=True):
             if e: e[4].record()
             moe.moe_combine(p, b["y"], b["pair_rows"], b["topk_weights"], b["out"])
             if e: e[5].record()
+            moe.moe_combine_residual(p, b["y"], b["pair_rows"], b["topk_weights"], gain, 1e-6, 2,
+                                     stream_res)
+            if e: e[6].record()
         torch.cuda.synchronize()
         kt = {}
         for j, nm in enumerate(names):
             kt[nm] = sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps
         res["kernel_ms"] = kt
     return res
+
+
+def run_dense(steps, warmup):
+    """The dense SwiGLU MLP (moe_dense_mlp) on its synthetic workload, timed
+    with events on the current stream."""
+    import torch
+
+    from group_limited_routing_router_amd import moe
+    from group_limited_routing_router_amd.inputs import CONFIGS, make_inputs
+
+    cfg = CONFIGS["dense"]
+    d = make_inputs(cfg, seed=0, device="cuda")
+    p = moe.MoEProblem.from_config(cfg)
+    ws = torch.empty(moe.moe_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
+
+    def step():
+        moe.moe_dense_mlp(p, d["x"], d["w_gate"], d["w_up"], d["w_down"], out, ws)
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 6 * cfg.T * cfg.H * cfg.I
+    bytes_ = 3 * cfg.I * cfg.H * 2 + cfg.T * cfg.H * 2 + cfg.T * cfg.H * 4
+    del d, ws, out
+    return {"tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+            "roofline": {"bound": "mfma", "achieved": round(flops / (ms * 1e-3) / 1e12, 1),
+                         "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
+                         "frac": round(flops / (ms * 1e-3) / PEAK_BF16, 4), "traffic": None,
+                         "algorithmic_bytes": bytes_, "algorithmic_flops": flops}}
 
 
 def roofline_for(res, kernel):
@@ -223,6 +271,8 @@ def main():
                     choices=["prefill", "decode", "skew", "long"])
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the secondary decode (T=128) measurement")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the secondary dense-MLP measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -258,7 +308,7 @@ def main():
     kms = main_res["kernel_ms"]
     log("[bench] %s T=%d: %.3f ms/step; kernels %s" % (
         cfg.name, cfg.T, main_res["ms"], {k: round(v, 4) for k, v in kms.items()}))
-    dominant = max(kms, key=kms.get)
+    dominant = max((k for k in kms if k != "combine_residual"), key=kms.get)
     layer = main_res["layer"]
     ms = main_res["ms"]
     out = {
@@ -282,8 +332,11 @@ def main():
                   "mfma_frac": round(layer["flops"] / (ms * 1e-3) / PEAK_BF16, 4),
                   "hbm_gbs": round(layer["bytes"] / (ms * 1e-3) / 1e9, 1),
                   "hbm_frac": round(layer["bytes"] / (ms * 1e-3) / PEAK_HBM, 4)},
-        "kernels_ms": {k: round(v, 4) for k, v in kms.items()},
+        "kernels_ms": {k: round(v, 4) for k, v in kms.items() if k != "combine_residual"},
         "roofline": roofline_for(main_res, dominant),
+        # the combine fused with the post-norm and residual update (not part of
+        # the timed step: a separate entry point after the block)
+        "combine_residual": roofline_for(main_res, "combine_residual"),
     }
     if not args.no_decode and args.workload != "decode":
         dec = run_workload("decode", args.steps, args.warmup, weights)
@@ -294,12 +347,19 @@ def main():
             "experts_hit": dec["n_hit"],
             "hbm_gbs": round(dl["bytes"] / (dec["ms"] * 1e-3) / 1e9, 1),
             "hbm_frac": round(dl["bytes"] / (dec["ms"] * 1e-3) / PEAK_HBM, 4),
-            "kernels_ms": {k: round(v, 4) for k, v in dec["kernel_ms"].items()},
-            "roofline": roofline_for(dec, max(dec["kernel_ms"], key=dec["kernel_ms"].get)),
+            "kernels_ms": {k: round(v, 4) for k, v in dec["kernel_ms"].items()
+                           if k != "combine_residual"},
+            "roofline": roofline_for(dec, max((k for k in dec["kernel_ms"] if k != "combine_residual"),
+                                              key=dec["kernel_ms"].get)),
         }
         log("[bench] decode T=128: %.3f ms/step, %.1f%% of HBM peak" % (
             dec["ms"], 100 * out["decode"]["hbm_frac"]))
         del dec
+    if not args.no_dense:
+        out["dense_mlp"] = run_dense(args.steps, args.warmup)
+        log("[bench] dense MLP T=%d I=%d: %.3f ms/step, %.1f%% of bf16 MFMA peak" % (
+            out["dense_mlp"]["tokens"], out["dense_mlp"]["intermediate"],
+            out["dense_mlp"]["ms_per_step"], 100 * out["dense_mlp"]["roofline"]["frac"]))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(main_res, args.cpu_seconds)
         log("[bench] cpu oracle: %s" % out["cpu_baseline"])

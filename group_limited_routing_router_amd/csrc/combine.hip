@@ -77,6 +77,102 @@ hipError_t launch_k(const Problem& p, const float* y, const int32_t* pair_rows,
     return hipGetLastError();
 }
 
+// Sublayer epilogue fused into the combine ("Welcome Beam: a 501B open model
+// you can own, customize, and scale", section "Residual Stream": every
+// sublayer output is normalised; step s of the stream adds it with weight
+// 1/sqrt(s) and keeps the stream with weight sqrt((s-1)/s); the norms run in
+// FP32).  The norm is RMSNorm with a per-channel gain.  The combined row o
+// stays in registers (NC float4 chunks per thread) between the sum of squares
+// and the update, so it never goes to memory.  The sum of squares is reduced
+// in a fixed order: per thread over its chunks, a shuffle tree in each wave,
+// then the waves in index order.
+template <int K, int NC>
+__global__ __launch_bounds__(kThreads) void combine_residual_kernel(
+    int64_t T, int H, float scale, const float* __restrict__ y,
+    const int32_t* __restrict__ pair_rows, const float* __restrict__ weights,
+    const float* __restrict__ gain, float eps, float wa, float wb, float* __restrict__ res) {
+    __shared__ float s_part[kThreads / 64];
+    const int64_t t = blockIdx.x;
+    int32_t row[K];
+    float w[K];
+#pragma unroll
+    for (int j = 0; j < K; ++j) {
+        row[j] = pair_rows[t * K + j];
+        w[j] = weights[t * K + j];
+    }
+    const int nv = H >> 2;
+    float4 o[NC];
+    float ss = 0.0f;
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+        o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (c < nv) {
+            float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+            for (int j = 0; j < K; ++j) {
+                if (row[j] < 0) continue;
+                const float4 v = reinterpret_cast<const float4*>(y + static_cast<int64_t>(row[j]) * H)[c];
+                acc.x = acc.x + w[j] * v.x;
+                acc.y = acc.y + w[j] * v.y;
+                acc.z = acc.z + w[j] * v.z;
+                acc.w = acc.w + w[j] * v.w;
+            }
+            acc.x *= scale;
+            acc.y *= scale;
+            acc.z *= scale;
+            acc.w *= scale;
+            o[i] = acc;
+            ss = ss + acc.x * acc.x;
+            ss = ss + acc.y * acc.y;
+            ss = ss + acc.z * acc.z;
+            ss = ss + acc.w * acc.w;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss = ss + __shfl_xor(ss, off);
+    if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = s_part[0];
+#pragma unroll
+    for (int i = 1; i < kThreads / 64; ++i) tot = tot + s_part[i];
+    const float inv = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
+    float4* r4 = reinterpret_cast<float4*>(res + t * H);
+    const float4* g4 = reinterpret_cast<const float4*>(gain);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+        const int c = threadIdx.x + i * kThreads;
+        if (c < nv) {
+            const float4 g = g4[c];
+            float4 r = r4[c];
+            r.x = wa * r.x + wb * ((o[i].x * inv) * g.x);
+            r.y = wa * r.y + wb * ((o[i].y * inv) * g.y);
+            r.z = wa * r.z + wb * ((o[i].z * inv) * g.z);
+            r.w = wa * r.w + wb * ((o[i].w * inv) * g.w);
+            r4[c] = r;
+        }
+    }
+}
+
+template <int K>
+hipError_t launch_residual_k(const Problem& p, const float* y, const int32_t* pair_rows,
+                             const float* weights, const float* gain, float eps, float wa,
+                             float wb, float* res, hipStream_t s) {
+    const dim3 grid(static_cast<unsigned>(p.T)), block(kThreads);
+    const int chunks = (p.H / 4 + kThreads - 1) / kThreads;
+#define MOE_RES(NC)                                                                       \
+    combine_residual_kernel<K, NC><<<grid, block, 0, s>>>(p.T, p.H, p.scale, y, pair_rows, \
+                                                          weights, gain, eps, wa, wb, res)
+    if (chunks <= 1) MOE_RES(1);
+    else if (chunks <= 2) MOE_RES(2);
+    else if (chunks <= 4) MOE_RES(4);
+    else if (chunks <= 8) MOE_RES(8);
+    else if (chunks <= kResidualMaxChunks) MOE_RES(16);
+    else return hipErrorInvalidValue;
+#undef MOE_RES
+    return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_combine(const Problem& p, const float* y, const int32_t* pair_rows,
@@ -84,6 +180,20 @@ hipError_t launch_combine(const Problem& p, const float* y, const int32_t* pair_
     switch (p.k) {
 #define MOE_CASE(K) \
     case K: return launch_k<K>(p, y, pair_rows, weights, out, out_bf16, s);
+        MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7)
+        MOE_CASE(8) MOE_CASE(9) MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13)
+        MOE_CASE(14) MOE_CASE(15) MOE_CASE(16)
+#undef MOE_CASE
+        default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_combine_residual(const Problem& p, const float* y, const int32_t* pair_rows,
+                                   const float* weights, const float* gain, float eps,
+                                   float wa, float wb, float* res, hipStream_t s) {
+    switch (p.k) {
+#define MOE_CASE(K) \
+    case K: return launch_residual_k<K>(p, y, pair_rows, weights, gain, eps, wa, wb, res, s);
         MOE_CASE(1) MOE_CASE(2) MOE_CASE(3) MOE_CASE(4) MOE_CASE(5) MOE_CASE(6) MOE_CASE(7)
         MOE_CASE(8) MOE_CASE(9) MOE_CASE(10) MOE_CASE(11) MOE_CASE(12) MOE_CASE(13)
         MOE_CASE(14) MOE_CASE(15) MOE_CASE(16)

@@ -26,6 +26,11 @@ hipError_t launch_permute(const Problem& p, const int32_t* ids, int32_t* offsets
                           int32_t* sorted_pairs, int32_t* pair_rows, int32_t* block_counts,
                           hipStream_t s);
 
+// sorted_pairs = 0 .. T-1 and offsets = {0, T}: the dispatch of one expert
+// that takes every token (a dense layer).
+hipError_t launch_identity_dispatch(int64_t T, int32_t* offsets, int32_t* sorted_pairs,
+                                    hipStream_t s);
+
 hipError_t launch_expert_ffn(const Problem& p, const uint16_t* x, const int32_t* sorted_pairs,
                              const int32_t* offsets, const uint16_t* w_gate,
                              const uint16_t* w_up, const uint16_t* w_down, uint16_t* h, float* y,
@@ -40,5 +45,15 @@ hipError_t launch_down(const Problem& p, const uint16_t* h, const int32_t* offse
 
 hipError_t launch_combine(const Problem& p, const float* y, const int32_t* pair_rows,
                           const float* weights, void* out, bool out_bf16, hipStream_t s);
+
+// Combine fused with the post-norm and residual update; the combined row is
+// held in registers, at most kResidualMaxChunks float4 chunks per thread of
+// 256, i.e. H <= 16384.
+constexpr int kResidualMaxChunks = 16;
+constexpr int kResidualMaxH = kResidualMaxChunks * 4 * 256;
+
+hipError_t launch_combine_residual(const Problem& p, const float* y, const int32_t* pair_rows,
+                                   const float* weights, const float* gain, float eps,
+                                   float wa, float wb, float* res, hipStream_t s);
 
 }  // namespace moe

@@ -228,6 +228,56 @@ MOE_EXPORT moe_status moe_combine(const moe_problem* p, const float* y, const in
                       "combine launch");
 }
 
+MOE_EXPORT moe_status moe_combine_residual(const moe_problem* p, const float* y,
+                                           const int32_t* pair_rows, const float* topk_weights,
+                                           const float* norm_weight, float eps, int32_t step,
+                                           float* residual, hipStream_t stream) {
+    MOE_TRY(check_problem(p));
+    if (!(eps > 0.0f) || !isfinite(eps))
+        return fail(MOE_ERR_INVALID_ARG, "eps=%g must be finite and > 0", (double)eps);
+    if (step < 1) return fail(MOE_ERR_INVALID_ARG, "step=%d must be >= 1", step);
+    if (p->H > moe::kResidualMaxH)
+        return fail(MOE_ERR_UNSUPPORTED, "H=%d > %d for the fused epilogue", p->H, moe::kResidualMaxH);
+    if (p->T == 0) return ok();
+    MOE_TRY(check_ptr(y, "y"));
+    MOE_TRY(check_ptr(pair_rows, "pair_rows"));
+    MOE_TRY(check_ptr(topk_weights, "topk_weights"));
+    MOE_TRY(check_ptr(norm_weight, "norm_weight"));
+    MOE_TRY(check_ptr(residual, "residual"));
+    // the stream weights in fp32, as the oracle takes them
+    const float wa = sqrtf(static_cast<float>(step - 1) / static_cast<float>(step));
+    const float wb = 1.0f / sqrtf(static_cast<float>(step));
+    return hip_status(moe::launch_combine_residual(to_internal(*p), y, pair_rows, topk_weights,
+                                                   norm_weight, eps, wa, wb, residual, stream),
+                      "combine/residual launch");
+}
+
+MOE_EXPORT moe_status moe_dense_mlp(const moe_problem* p, const moe_bf16* x,
+                                    const moe_bf16* w_gate, const moe_bf16* w_up,
+                                    const moe_bf16* w_down, float* out, void* ws, size_t ws_bytes,
+                                    hipStream_t stream) {
+    MOE_TRY(check_problem(p));
+    if (p->E != 1 || p->G != 1 || p->TG != 1 || p->k != 1)
+        return fail(MOE_ERR_INVALID_ARG, "a dense MLP needs E=G=TG=k=1 (got E=%d G=%d TG=%d k=%d)",
+                    p->E, p->G, p->TG, p->k);
+    if (p->T == 0) return ok();
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(w_gate, "w_gate"));
+    MOE_TRY(check_ptr(w_up, "w_up"));
+    MOE_TRY(check_ptr(w_down, "w_down"));
+    MOE_TRY(check_ptr(out, "out"));
+    MOE_TRY(check_ws(*p, ws, ws_bytes));
+    const Layout L = layout_of(*p);
+    const moe::Problem q = to_internal(*p);
+    int32_t* off = at<int32_t>(ws, L.offsets);
+    int32_t* sorted = at<int32_t>(ws, L.sorted);
+    hipError_t e = moe::launch_identity_dispatch(p->T, off, sorted, stream);
+    if (e != hipSuccess) return hip_status(e, "dispatch launch");
+    e = moe::launch_expert_ffn(q, x, sorted, off, w_gate, w_up, w_down, at<uint16_t>(ws, L.h), out,
+                               stream);
+    return hip_status(e, "dense mlp launch");
+}
+
 MOE_EXPORT moe_status moe_forward(const moe_problem* p, const moe_bf16* x,
                                   const moe_bf16* w_router, const float* bias,
                                   const moe_bf16* w_gate, const moe_bf16* w_up,

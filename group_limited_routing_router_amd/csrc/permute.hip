@@ -135,4 +135,27 @@ hipError_t launch_permute(const Problem& p, const int32_t* ids, int32_t* offsets
     return hipGetLastError();
 }
 
+namespace {
+
+// The dispatch of a dense layer: one expert owns every row, row q is token q.
+__global__ __launch_bounds__(kThreads) void identity_dispatch_kernel(int64_t T, int32_t* offsets,
+                                                                     int32_t* sorted_pairs) {
+    const int64_t i = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+    if (i < T) sorted_pairs[i] = static_cast<int32_t>(i);
+    if (i == 0) {
+        offsets[0] = 0;
+        offsets[1] = static_cast<int32_t>(T);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_identity_dispatch(int64_t T, int32_t* offsets, int32_t* sorted_pairs,
+                                    hipStream_t s) {
+    const int64_t grid = T > 0 ? (T + kThreads - 1) / kThreads : 1;
+    identity_dispatch_kernel<<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s>>>(
+        T, offsets, sorted_pairs);
+    return hipGetLastError();
+}
+
 }  // namespace moe

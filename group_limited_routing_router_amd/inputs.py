@@ -55,6 +55,10 @@ CONFIGS = {
     "skew": MoEConfig("skew", T=4096, hot_groups=2, hot_per_group=8, hot_bias=3.0, **_BEAM),
     # long prefill processed as one call
     "long": MoEConfig("long", T=65536, **_BEAM),
+    # dense SwiGLU MLP of the first layers on the expert kernels (one expert
+    # takes every token); the pages do not give its intermediate size, so it is
+    # taken as the width of the eight experts a token runs, 8 * 2560
+    "dense": MoEConfig("dense", T=8192, H=5120, I=20480, E=1, G=1, TG=1, k=1, scale=1.0),
 }
 
 ACT_STD = 1.0

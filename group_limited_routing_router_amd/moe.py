@@ -49,8 +49,8 @@ class MoEProblem(ctypes.Structure):
 
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
-           "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_forward",
-           "moe_status_string", "moe_last_error")
+           "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_combine_residual",
+           "moe_dense_mlp", "moe_forward", "moe_status_string", "moe_last_error")
 
 
 def library_path() -> str:
@@ -100,6 +100,11 @@ def load_library():
         lib.moe_expert_down.restype = st
         lib.moe_combine.argtypes = [prob, P, P, P, P, ctypes.c_int, P]
         lib.moe_combine.restype = st
+        lib.moe_combine_residual.argtypes = [prob, P, P, P, P, ctypes.c_float, ctypes.c_int32, P,
+                                             P]
+        lib.moe_combine_residual.restype = st
+        lib.moe_dense_mlp.argtypes = [prob, P, P, P, P, P, P, ctypes.c_size_t, P]
+        lib.moe_dense_mlp.restype = st
         lib.moe_forward.argtypes = [prob, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, P,
                                     ctypes.c_size_t, P]
         lib.moe_forward.restype = st
@@ -179,6 +184,19 @@ def moe_expert_down(p, h, expert_offsets, w_down, y, stream=None):
 def moe_combine(p, y, pair_rows, topk_weights, out, stream=None):
     _check(load_library().moe_combine(ctypes.byref(p), _p(y), _p(pair_rows), _p(topk_weights),
                                        _p(out), _dtype_code(out), _stream(stream)))
+
+
+def moe_combine_residual(p, y, pair_rows, topk_weights, norm_weight, eps, step, residual,
+                         stream=None):
+    _check(load_library().moe_combine_residual(ctypes.byref(p), _p(y), _p(pair_rows),
+                                                _p(topk_weights), _p(norm_weight), float(eps),
+                                                int(step), _p(residual), _stream(stream)))
+
+
+def moe_dense_mlp(p, x, w_gate, w_up, w_down, out, ws, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().moe_dense_mlp(ctypes.byref(p), _p(x), _p(w_gate), _p(w_up), _p(w_down),
+                                         _p(out), _p(ws), nbytes, _stream(stream)))
 
 
 def moe_forward(p, x, w_router, bias, w_gate, w_up, w_down, out, topk_ids, topk_weights, y, ws,

@@ -145,6 +145,41 @@ moe_status moe_combine(const moe_problem* p, const float* y, const int32_t* pair
                        const float* topk_weights, void* out, moe_dtype out_dtype,
                        hipStream_t stream);
 
+/* The combine fused with the sublayer epilogue that follows it ("Welcome Beam:
+ * a 501B open model you can own, customize, and scale", section "Residual
+ * Stream": every sublayer output is normalised; the embedding is step 1 of
+ * the residual stream and step s adds the normalised output with weight
+ * 1/sqrt(s) while the stream keeps weight sqrt((s-1)/s); the norms compute in
+ * FP32).  The norm is RMSNorm with a per-channel gain.
+ *   y, pair_rows, topk_weights   as for moe_combine
+ *   norm_weight  [H] fp32 gain g
+ *   eps          > 0, added to the mean square
+ *   step         s >= 1 (s = 1 replaces the stream)
+ *   residual     [T,H] fp32, updated in place:
+ *                o        = the fp32 row moe_combine would write for token t
+ *                res[t,m] = sqrt((s-1)/s) * res[t,m]
+ *                           + (1/sqrt(s)) * g[m] * o[m] / sqrt(mean(o^2) + eps)
+ * The combined output itself is not written.  H <= 16384 (else
+ * MOE_ERR_UNSUPPORTED).  The sum of squares is reduced in a fixed order, so
+ * the result is deterministic. */
+moe_status moe_combine_residual(const moe_problem* p, const float* y, const int32_t* pair_rows,
+                                const float* topk_weights, const float* norm_weight, float eps,
+                                int32_t step, float* residual, hipStream_t stream);
+
+/* Dense SwiGLU MLP on the expert kernels ("Welcome Beam: a 501B open model you
+ * can own, customize, and scale", section "Mixture of Experts": the first
+ * layers use a dense SwiGLU MLP instead of the expert block).
+ *   p         E = G = TG = k = 1 (else MOE_ERR_INVALID_ARG); scale unused;
+ *             I is the MLP's intermediate size
+ *   x         [T,H] bf16
+ *   w_gate, w_up  [I,H] bf16;  w_down [H,I] bf16
+ *   out       [T,H] fp32: out[t] = bf16(silu(x_t . w_gate^T) * (x_t . w_up^T))
+ *             . w_down^T, the same arithmetic as one expert of moe_expert_ffn
+ *   ws        moe_workspace_bytes(p) bytes (holds the bf16 product [T,I]) */
+moe_status moe_dense_mlp(const moe_problem* p, const moe_bf16* x, const moe_bf16* w_gate,
+                         const moe_bf16* w_up, const moe_bf16* w_down, float* out, void* ws,
+                         size_t ws_bytes, hipStream_t stream);
+
 /* The whole block: route, permute, expert FFN, combine.
  *   topk_ids, topk_weights  optional [T,k] outputs (NULL: kept in `ws`)
  *   y                       [T*k,H] fp32 caller buffer for expert outputs

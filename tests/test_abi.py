@@ -107,6 +107,35 @@ def test_pointer_and_workspace_errors(lib):
                             guard.ctypes.data, 0, None, None, None, good, need, None) == 1
     assert np.all(guard == 3)
     assert cdll.moe_status_string(3) == b"MOE_ERR_WORKSPACE"
+    # fused epilogue: eps, step, missing pointers, hidden size beyond the limit
+    f, i32 = ctypes.c_float, ctypes.c_int32
+    assert cdll.moe_combine_residual(ctypes.byref(p), good, good, good, good, f(0.0), i32(2),
+                                     good, None) == 1
+    assert b"eps" in cdll.moe_last_error()
+    assert cdll.moe_combine_residual(ctypes.byref(p), good, good, good, good, f(float("nan")),
+                                     i32(2), good, None) == 1
+    assert cdll.moe_combine_residual(ctypes.byref(p), good, good, good, good, f(1e-6), i32(0),
+                                     good, None) == 1
+    assert b"step" in cdll.moe_last_error()
+    assert cdll.moe_combine_residual(ctypes.byref(p), good, good, good, None, f(1e-6), i32(2),
+                                     good, None) == 1
+    assert b"norm_weight" in cdll.moe_last_error()
+    assert cdll.moe_combine_residual(ctypes.byref(p), good, good, good, good, f(1e-6), i32(2),
+                                     odd, None) == 1
+    # dense MLP: needs one expert, one group, k = 1, and a workspace
+    assert cdll.moe_dense_mlp(ctypes.byref(p), good, good, good, good, good, good, need,
+                              None) == 1
+    assert b"E=G=TG=k=1" in cdll.moe_last_error()
+    dense = _beam()
+    dense.E = dense.G = dense.TG = dense.k = 1
+    assert cdll.moe_dense_mlp(ctypes.byref(dense), good, good, good, good, good, None, 0,
+                              None) == 3
+    assert cdll.moe_dense_mlp(ctypes.byref(dense), good, good, None, good, good, good, 1 << 40,
+                              None) == 1
+    wide = _beam()
+    wide.H = 16384 + 128
+    assert cdll.moe_combine_residual(ctypes.byref(wide), good, good, good, good, f(1e-6), i32(2),
+                                     good, None) == 2
 
 
 def test_zero_tokens_is_a_noop(lib):
@@ -117,6 +146,12 @@ def test_zero_tokens_is_a_noop(lib):
     assert cdll.moe_expert_ffn(ctypes.byref(p), None, None, None, None, None, None, None, None,
                                0, None) == 0
     assert cdll.moe_combine(ctypes.byref(p), None, None, None, None, 0, None) == 0
+    assert cdll.moe_combine_residual(ctypes.byref(p), None, None, None, None, ctypes.c_float(1e-6),
+                                     ctypes.c_int32(3), None, None) == 0
+    dense = _beam(0)
+    dense.E = dense.G = dense.TG = dense.k = 1
+    assert cdll.moe_dense_mlp(ctypes.byref(dense), None, None, None, None, None, None, 0,
+                              None) == 0
     assert cdll.moe_forward(ctypes.byref(p), None, None, None, None, None, None, None, 0, None,
                             None, None, None, 0, None) == 0
 

@@ -1,0 +1,61 @@
+"""GPU parity of the dense SwiGLU MLP (moe_dense_mlp: one expert that takes
+every token, on the expert kernels) against the oracle's SwiGLU expert.
+
+Small shapes are compared on every output; wide ones on seeded sampled tokens
+that the oracle computes one by one.  The shapes reach the 16-row, 64-row and
+large-tile kernels and a ragged last row tile."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from group_limited_routing_router_amd.inputs import MoEConfig, bits, make_inputs
+
+from _parity import OUT_TOL, out_error
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from group_limited_routing_router_amd import moe as m
+    m.load_library()
+    return m
+
+
+CASES = [
+    # (T, H, I, sampled tokens or 0 for all)
+    (20, 256, 128, 0),        # 16-row tiles
+    (64, 512, 256, 0),        # 64-row tiles
+    (300, 512, 384, 0),       # large tiles with a ragged second row tile
+    (1000, 256, 1024, 0),
+    (2048, 5120, 2048, 24),   # Beam width, large tiles, sampled
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "T%d_H%d_I%d" % c[:3])
+def test_dense_mlp(moe, case):
+    T, H, I, nsample = case
+    print(f"[case] dense_mlp T={T} H={H} I={I}", flush=True)
+    cfg = MoEConfig("dense", T=T, H=H, I=I, E=1, G=1, TG=1, k=1, scale=1.0)
+    d = make_inputs(cfg, seed=5)
+    g = {kk: v.cuda() for kk, v in d.items()}
+    p = moe.MoEProblem.from_config(cfg)
+    ws = torch.empty(moe.moe_workspace_bytes(p), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    moe.moe_dense_mlp(p, g["x"], g["w_gate"], g["w_up"], g["w_down"], out, ws)
+    out2 = torch.empty_like(out)
+    moe.moe_dense_mlp(p, g["x"], g["w_gate"], g["w_up"], g["w_down"], out2, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2), "dense MLP is not deterministic"
+    got = out.cpu().numpy()
+    if nsample:
+        tok = np.sort(np.random.default_rng(7).choice(T, nsample, replace=False)).astype(np.int32)
+    else:
+        tok = np.arange(T, dtype=np.int32)
+    want, _ = oracle.ffn_pairs(tok, np.zeros_like(tok), bits(d["x"]), bits(d["w_gate"]),
+                               bits(d["w_up"]), bits(d["w_down"]))
+    err, rms = out_error(got[tok], want)
+    print(f"    err/rms={err:.2e} (rms {rms:.3f}) on {len(tok)} tokens", flush=True)
+    assert err <= OUT_TOL
