@@ -120,6 +120,41 @@ def make_weights(cfg: MoEConfig, seed: int = 0, device="cpu"):
     return dict(w_router=w_router, w_gate=w_gate, w_up=w_up, w_down=w_down)
 
 
+E4M3_MAX = 448.0  # largest finite FP8 E4M3 (OCP e4m3fn) value
+
+
+def quantize_rows_e4m3(w: torch.Tensor, chunk: int = 8):
+    """An FP8 copy of a stack of weight matrices [E, rows, cols]: one fp32 scale
+    per row (its largest magnitude over 448, 1 for an all-zero row) and the E4M3
+    codes of w / scale as uint8, both from torch's own float8_e4m3fn cast
+    (round to nearest even).  Done in chunks of `chunk` matrices."""
+    E, R, C = w.shape
+    codes = torch.empty((E, R, C), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((E, R), dtype=torch.float32, device=w.device)
+    for a in range(0, E, chunk):
+        b = min(E, a + chunk)
+        wf = w[a:b].float()
+        amax = wf.abs().amax(dim=2)
+        sc = torch.where(amax > 0, amax / E4M3_MAX, torch.ones_like(amax))
+        codes[a:b] = (wf / sc[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+        scales[a:b] = sc
+        del wf
+    return codes, scales
+
+
+def make_weights_fp8(cfg: MoEConfig, seed: int = 0, device="cpu"):
+    """The router weight of make_weights and an FP8 copy of its expert stacks
+    (quantize_rows_e4m3): q_gate/q_up [E,I,H], q_down [E,H,I] uint8 codes with
+    s_gate/s_up [E,I] and s_down [E,H] fp32 scales.  The bf16 expert weights are
+    drawn exactly as make_weights draws them and then dropped."""
+    w = make_weights(cfg, seed, device)
+    out = dict(w_router=w.pop("w_router"))
+    for name in ("gate", "up", "down"):
+        q, s = quantize_rows_e4m3(w.pop("w_" + name))
+        out["q_" + name], out["s_" + name] = q, s
+    return out
+
+
 def make_inputs(cfg: MoEConfig, seed: int = 0, device="cpu"):
     """Tokens and weights of one workload: x, bias, w_router, w_gate, w_up,
     w_down (see make_tokens and make_weights)."""

@@ -22,8 +22,11 @@ SwiGLU expert by ``torch.nn.functional`` on the CPU; the combine by the k=1
 and identical-experts closed forms; the whole block by the dense all-experts
 sum when k=E and G=1; the sublayer epilogue (``residual_norm``) by
 ``torch.nn.functional.rms_norm`` at step 1 and by the closed forms of the
-stream update (scale of the stream, zero stream, orthogonal inputs).  No
-function here is parity-unpinned.
+stream update (scale of the stream, zero stream, orthogonal inputs); the FP8
+expert (``ffn_pairs_fp8``) by torch's float8_e4m3fn decoding of every code
+and by bit equality with the bf16 expert when every channel scale is a power
+of two (the scaled weights are then exact in bf16).  No function here is
+parity-unpinned.
 """
 from __future__ import annotations
 
@@ -73,6 +76,10 @@ def _load():
         lib.oracle_permute.restype = ctypes.c_int
         lib.oracle_ffn_pairs.argtypes = [i64, i32, i32, P, P, P, P, P, P, P, P]
         lib.oracle_ffn_pairs.restype = ctypes.c_int
+        lib.oracle_ffn_pairs_fp8.argtypes = [i64, i32, i32, P, P, P, P, P, P, P, P, P, P, P]
+        lib.oracle_ffn_pairs_fp8.restype = ctypes.c_int
+        lib.oracle_e4m3_decode.argtypes = [i64, P, P]
+        lib.oracle_e4m3_decode.restype = None
         lib.oracle_combine.argtypes = [i64, i32, i32, P, P, f32, P]
         lib.oracle_combine.restype = ctypes.c_int
         lib.oracle_residual_norm.argtypes = [i64, i32, P, P, f32, i32, P]
@@ -167,6 +174,49 @@ def ffn_pairs(tok, exp, x, w_gate, w_up, w_down, want_h=False):
     _check(lib.oracle_ffn_pairs(n, H, I, _ptr(tok), _ptr(exp), _ptr(x), _ptr(w_gate),
                                 _ptr(w_up), _ptr(w_down), _ptr(h), _ptr(y)), "ffn")
     return y, h
+
+
+def ffn_pairs_fp8(tok, exp, x, q_gate, s_gate, q_up, s_up, q_down, s_down, want_h=False):
+    """ffn_pairs with FP8 (E4M3 codes, uint8) weights and fp32 per-channel
+    scales: q_gate/q_up [*,I,H], s_gate/s_up [*,I], q_down [*,H,I], s_down [*,H]."""
+    lib = _load()
+    tok = _c(tok, np.int32).ravel()
+    exp = _c(exp, np.int32).ravel()
+    x = _c(x, np.uint16)
+    qg, qu, qd = _c(q_gate, np.uint8), _c(q_up, np.uint8), _c(q_down, np.uint8)
+    sg, su, sd = _c(s_gate, np.float32), _c(s_up, np.float32), _c(s_down, np.float32)
+    n = tok.shape[0]
+    H = x.shape[1]
+    I = qg.shape[1]
+    assert qg.shape[2] == H and qd.shape[1:] == (H, I) and sg.shape == qg.shape[:2]
+    assert sd.shape == qd.shape[:2]
+    y = np.empty((n, H), np.float32)
+    h = np.empty((n, I), np.uint16) if want_h else None
+    _check(lib.oracle_ffn_pairs_fp8(n, H, I, _ptr(tok), _ptr(exp), _ptr(x), _ptr(qg), _ptr(sg),
+                                    _ptr(qu), _ptr(su), _ptr(qd), _ptr(sd), _ptr(h), _ptr(y)),
+           "ffn_pairs_fp8")
+    return y, h
+
+
+def forward_with_routing_fp8(x, ids, weights, q_gate, s_gate, q_up, s_up, q_down, s_down,
+                             scale, want_h=False):
+    """FP8-weight expert FFN and combine for given routing (ids, weights) [T,k]."""
+    ids = _c(ids, np.int32)
+    T, k = ids.shape
+    tok = np.repeat(np.arange(T, dtype=np.int32), k)
+    y, h = ffn_pairs_fp8(tok, ids.ravel(), x, q_gate, s_gate, q_up, s_up, q_down, s_down,
+                         want_h=want_h)
+    out = combine(y, weights, scale)
+    return out, y, h
+
+
+def e4m3_decode(codes):
+    """The oracle's decoding of E4M3 codes (uint8) to float32."""
+    lib = _load()
+    c = _c(codes, np.uint8)
+    out = np.empty(c.shape, np.float32)
+    lib.oracle_e4m3_decode(c.size, _ptr(c), _ptr(out))
+    return out
 
 
 def combine(y, weights, scale):

@@ -269,6 +269,79 @@ int oracle_ffn_pairs(int64_t npairs, int32_t H, int32_t I, const int32_t* tok,
     return ORACLE_OK;
 }
 
+/* ---- FP8 expert weights ------------------------------------------------------
+ * The pages give no FP8 scheme for the experts; the reading taken: each weight
+ * matrix is stored as FP8 E4M3 codes (the OCP "e4m3fn" encoding: 1 sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits, no infinities, 0x7f/0xff NaN)
+ * with one fp32 scale per output channel (per row n of Wg/Wu, per row m of
+ * Wd).  A channel's dot product is its scale times the dot product with the
+ * decoded codes; activations and the SwiGLU product stay as in the bf16 path.
+ *   g[n] = sg[n] * sum_h x[h] q_g[n,h]   (the sum in fp32, h order)
+ *   u[n] = su[n] * sum_h x[h] q_u[n,h]
+ *   h[n] = bf16_rne((g[n] * sigmoid(g[n])) * u[n])
+ *   y[m] = sd[m] * sum_n h[n] q_d[m,n]  */
+static float e4m3_to_float(uint8_t b) {
+    const int sign = b >> 7, e = (b >> 3) & 15, m = b & 7;
+    float v;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0)
+        v = ldexpf((float)m, -9);            /* subnormal: m/8 * 2^-6 */
+    else
+        v = ldexpf((float)(8 + m), e - 10);  /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+static void swiglu_expert_one_token_fp8(int32_t H, int32_t I, const uint16_t* xrow,
+                                        const uint8_t* qg, const float* sg, const uint8_t* qu,
+                                        const float* su, const uint8_t* qd, const float* sd,
+                                        uint16_t* hbits, float* y) {
+    for (int32_t n = 0; n < I; ++n) {
+        const uint8_t* grow = qg + (int64_t)n * H;
+        const uint8_t* urow = qu + (int64_t)n * H;
+        float g = 0.0f, u = 0.0f;
+        for (int32_t c = 0; c < H; ++c) {
+            float xv = bf16_bits_to_float(xrow[c]);
+            g = g + xv * e4m3_to_float(grow[c]);
+            u = u + xv * e4m3_to_float(urow[c]);
+        }
+        g = sg[n] * g;
+        u = su[n] * u;
+        float silu = g * sigmoidf_plain(g);
+        hbits[n] = float_to_bf16_bits_rne(silu * u);
+    }
+    for (int32_t m = 0; m < H; ++m) {
+        const uint8_t* drow = qd + (int64_t)m * I;
+        float acc = 0.0f;
+        for (int32_t n = 0; n < I; ++n)
+            acc = acc + bf16_bits_to_float(hbits[n]) * e4m3_to_float(drow[n]);
+        y[m] = sd[m] * acc;
+    }
+}
+
+/* As oracle_ffn_pairs with FP8 weights: qg/qu [*,I,H] and qd [*,H,I] E4M3
+ * codes, sg/su [*,I] and sd [*,H] fp32 per-channel scales. */
+int oracle_ffn_pairs_fp8(int64_t npairs, int32_t H, int32_t I, const int32_t* tok,
+                         const int32_t* exp, const uint16_t* x, const uint8_t* qg,
+                         const float* sg, const uint8_t* qu, const float* su, const uint8_t* qd,
+                         const float* sd, uint16_t* h_out, float* y) {
+    if (npairs < 0 || H <= 0 || I <= 0) return ORACLE_ERR_ARG;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t q = 0; q < npairs; ++q) {
+        const int64_t e = exp[q];
+        uint16_t* hb = h_out ? h_out + q * I : (uint16_t*)malloc(sizeof(uint16_t) * (size_t)I);
+        swiglu_expert_one_token_fp8(H, I, x + (int64_t)tok[q] * H, qg + e * I * H, sg + e * I,
+                                    qu + e * I * H, su + e * I, qd + e * H * I, sd + e * H, hb,
+                                    y + q * H);
+        if (!h_out) free(hb);
+    }
+    return ORACLE_OK;
+}
+
+/* Exposed for the test that pins the decoding against a library cast. */
+void oracle_e4m3_decode(int64_t n, const uint8_t* src, float* dst) {
+    for (int64_t i = 0; i < n; ++i) dst[i] = e4m3_to_float(src[i]);
+}
+
 /* ---- recombination ----------------------------------------------------------
  * out[t,m] = scale * sum_j w[t,j] * y[t*k+j, m], the sum in j order, fp32.
  * y rows are in pair order (p = t*k+j). */
