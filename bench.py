@@ -136,6 +136,46 @@ def run_workload(name, steps, warmup, weights, want_kernels=True):
     return res
 
 
+def run_fp8(name, steps, warmup, weights_fp8):
+    """The block with FP8 expert weights (moe_forward_fp8) on a workload, timed
+    with events on the current stream; algorithmic bytes count one byte per
+    weight plus the per-channel scales."""
+    import torch
+
+    from group_limited_routing_router_amd import moe
+    from group_limited_routing_router_amd.inputs import CONFIGS, make_tokens
+
+    cfg = CONFIGS[name]
+    d = make_tokens(cfg, seed=0, device="cuda")
+    w = weights_fp8
+    p = moe.MoEProblem.from_config(cfg)
+    b = moe.alloc_buffers(p)
+
+    def step():
+        moe.moe_forward_fp8(p, d["x"], w["w_router"], d["bias"], w["q_gate"], w["s_gate"],
+                            w["q_up"], w["s_up"], w["q_down"], w["s_down"], b["out"],
+                            b["topk_ids"], b["topk_weights"], b["y"], b["ws"])
+
+    for _ in range(warmup):
+        step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    n_hit = int((torch.bincount(b["topk_ids"].flatten().long(), minlength=cfg.E) > 0).sum())
+    T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
+    flops = 2 * T * H * E + 6 * T * k * H * I
+    bytes_ = n_hit * (3 * I * H + (2 * I + H) * 4) + E * H * 2 + T * H * 2 + T * H * 4
+    return {"tokens": T, "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "experts_hit": n_hit, "hbm_gbs": round(bytes_ / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(bytes_ / (ms * 1e-3) / PEAK_HBM, 4),
+            "mfma_frac": round(flops / (ms * 1e-3) / PEAK_BF16, 4)}
+
+
 def run_dense(steps, warmup):
     """The dense SwiGLU MLP (moe_dense_mlp) on its synthetic workload, timed
     with events on the current stream."""
@@ -271,6 +311,8 @@ def main():
                     choices=["prefill", "decode", "skew", "long"])
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the secondary decode (T=128) measurement")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the secondary FP8-weight measurements")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the secondary dense-MLP measurement")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -355,6 +397,15 @@ def main():
         log("[bench] decode T=128: %.3f ms/step, %.1f%% of HBM peak" % (
             dec["ms"], 100 * out["decode"]["hbm_frac"]))
         del dec
+    if not args.no_fp8:
+        from group_limited_routing_router_amd.inputs import make_weights_fp8
+        w8 = make_weights_fp8(CONFIGS["decode"], seed=0, device="cuda")
+        out["fp8_weights"] = {n: run_fp8(n, args.steps, args.warmup, w8)
+                              for n in ("decode", args.workload)}
+        log("[bench] fp8 weights: %s" % {n: (v["ms_per_step"], v["hbm_frac"])
+                                          for n, v in out["fp8_weights"].items()})
+        del w8
+        torch.cuda.empty_cache()
     if not args.no_dense:
         out["dense_mlp"] = run_dense(args.steps, args.warmup)
         log("[bench] dense MLP T=%d I=%d: %.3f ms/step, %.1f%% of bf16 MFMA peak" % (

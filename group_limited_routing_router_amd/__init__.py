@@ -8,7 +8,8 @@ can be imported without a GPU or a built library.
 
 _BINDING_NAMES = (
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down",
-    "moe_combine", "moe_combine_residual", "moe_dense_mlp", "moe_forward",
+    "moe_combine", "moe_combine_residual", "moe_dense_mlp", "moe_expert_ffn_fp8", "moe_forward",
+    "moe_forward_fp8",
     "moe_workspace_bytes", "MoEProblem", "MoEError", "DTYPE_F32", "DTYPE_BF16",
     "load_library", "library_path",
 )

@@ -67,9 +67,11 @@ struct FfnArgs {
     const uint16_t* a_src;   // x [T,H] (gate/up) or h [P,I] (down)
     const int32_t* sorted_pairs;
     const int32_t* offsets;  // [E+1]
-    const uint16_t* b0;      // w_gate [E,I,H] or w_down [E,H,I]
-    const uint16_t* b1;      // w_up [E,I,H] (gate/up only)
+    const void* b0;          // w_gate [E,I,H] or w_down [E,H,I]: bf16, or FP8 E4M3 codes
+    const void* b1;          // w_up [E,I,H] (gate/up only)
     void* out;               // h [P,I] bf16 (gate/up) or y [P,H] fp32 (down)
+    const float* s0;         // FP8 weights only: per-channel scales of b0 [E,N]
+    const float* s1;         // and of b1
 };
 
 // Map this workgroup to a tile (expert e, column tile nt, row range
@@ -134,7 +136,28 @@ __device__ bool find_tile(const FfnArgs& a, int ncol_tiles, int32_t* s_off, int3
     return true;
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
+// FP8 E4M3 codes -> bf16, eight at a time: the hardware conversion to fp32 is
+// exact (and follows the OCP e4m3fn encoding on gfx950) and every E4M3 value
+// is a bf16 value, so the upper half of each fp32 is the bf16.
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    u32x4 r;
+    const uint32_t w[2] = {lo, hi};
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
+        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
+        r[2 * i] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
+        r[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
+    }
+    return as_bf16x8(r);
+}
+
+// FP8 = true: the weights are E4M3 codes with one fp32 scale per output
+// channel (FfnArgs::s0/s1).  They are staged in LDS as codes (64 bytes a row
+// and stage), widened to bf16 as each MFMA operand is read, and the channel
+// scale multiplies the fp32 accumulator in the epilogue.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP, bool FP8 = false>
 __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     static_assert(WAVES_M * WAVES_N == kWaves, "4 waves");
     constexpr int BN_OUT = GATEUP ? BN / 2 : BN;     // output columns per tile
@@ -143,14 +166,18 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     constexpr int WN_OUT = BN_OUT / WAVES_N;          // output columns per wave
     constexpr int NB = WN_OUT / 16;
     static_assert(MB >= 1 && NB >= 1, "tile too small");
+    constexpr int EB = FP8 ? 1 : 2;                   // bytes per weight
+    constexpr int B_ROW = BK * EB;                    // weight bytes per row and stage
+    constexpr int B_STRIDE = B_ROW + 16;              // LDS row pitch of the weight stage
+    constexpr int B_CPR = B_ROW / 16;                 // 16-byte chunks per weight row
     constexpr int A_CHUNKS = BM * (BK / 8);           // 16-byte chunks per stage
-    constexpr int B_CHUNKS = BN * (BK / 8);
+    constexpr int B_CHUNKS = BN * B_CPR;
     constexpr int A_ITERS = (A_CHUNKS + kThreads - 1) / kThreads;
     constexpr int B_ITERS = B_CHUNKS / kThreads;
     static_assert(B_CHUNKS % kThreads == 0, "B tile");
 
     __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * LDS_STRIDE];
-    __shared__ __attribute__((aligned(16))) uint16_t s_b[2][BN * LDS_STRIDE];
+    __shared__ __attribute__((aligned(16))) unsigned char s_b[2][BN * B_STRIDE];
     __shared__ int32_t s_off[kMaxE + 1];
     __shared__ int32_t s_tstart[kMaxE + 1];
 
@@ -179,12 +206,12 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
         }
         a_ptr[i] = a.a_src + src_row * K + (c & 7) * 8;
     }
-    const uint16_t* b_ptr[B_ITERS];
+    const unsigned char* b_ptr[B_ITERS];
 #pragma unroll
     for (int i = 0; i < B_ITERS; ++i) {
         const int c = tid + i * kThreads;
-        const int r = c >> 3;
-        const uint16_t* base;
+        const int r = c / B_CPR;
+        const void* base;
         int col;
         if constexpr (GATEUP) {
             base = r < BN_OUT ? a.b0 : a.b1;
@@ -193,7 +220,8 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
             base = a.b0;
             col = n0 + r;
         }
-        b_ptr[i] = base + (static_cast<int64_t>(e) * a.N + col) * K + (c & 7) * 8;
+        b_ptr[i] = static_cast<const unsigned char*>(base) +
+                   ((static_cast<int64_t>(e) * a.N + col) * K) * EB + (c % B_CPR) * 16;
     }
 
     u32x4 ra[A_ITERS], rb[B_ITERS];
@@ -203,7 +231,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
         for (int i = 0; i < A_ITERS; ++i)
             if (A_CHUNKS % kThreads == 0 || tid + i * kThreads < A_CHUNKS) ra[i] = ld16(a_ptr[i] + koff);
 #pragma unroll
-        for (int i = 0; i < B_ITERS; ++i) rb[i] = ld16(b_ptr[i] + koff);
+        for (int i = 0; i < B_ITERS; ++i) rb[i] = ld16(b_ptr[i] + koff * EB);
     };
     auto store_lds = [&](int buf) {
 #pragma unroll
@@ -215,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
 #pragma unroll
         for (int i = 0; i < B_ITERS; ++i) {
             const int c = tid + i * kThreads;
-            *reinterpret_cast<u32x4*>(&s_b[buf][(c >> 3) * LDS_STRIDE + (c & 7) * 8]) = rb[i];
+            *reinterpret_cast<u32x4*>(&s_b[buf][(c / B_CPR) * B_STRIDE + (c % B_CPR) * 16]) = rb[i];
         }
     };
 
@@ -238,7 +266,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
         const int buf = kt & 1;
         if (kt + 1 < nk) load_global(kt + 1);
         const uint16_t* sa = s_a[buf];
-        const uint16_t* sb = s_b[buf];
+        const unsigned char* sb = s_b[buf];
 #pragma unroll
         for (int ks = 0; ks < BK / 32; ++ks) {
             const int kof = ks * 32 + q * 8;
@@ -251,7 +279,14 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
 #pragma unroll
                 for (int n = 0; n < NB; ++n) {
                     const int brow = g * BN_OUT + wn * WN_OUT + n * 16 + r16;
-                    const bf16x8 bfr = *reinterpret_cast<const bf16x8*>(&sb[brow * LDS_STRIDE + kof]);
+                    bf16x8 bfr;
+                    if constexpr (FP8) {
+                        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                        const u32x2 w8 = *reinterpret_cast<const u32x2*>(&sb[brow * B_STRIDE + kof]);
+                        bfr = e4m3x8_to_bf16x8(w8[0], w8[1]);
+                    } else {
+                        bfr = *reinterpret_cast<const bf16x8*>(&sb[brow * B_STRIDE + kof * 2]);
+                    }
 #pragma unroll
                     for (int m = 0; m < MB; ++m) acc[g][m][n] = mfma16(af[m], bfr, acc[g][m][n]);
                 }
@@ -262,6 +297,13 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     }
 
     // ---- epilogue ----
+    float sc0[NB], sc1[NB];  // per-channel scales of this lane's columns (FP8)
+#pragma unroll
+    for (int n = 0; n < NB; ++n) {
+        const int64_t ch = static_cast<int64_t>(e) * a.N + n0 + wn * WN_OUT + n * 16 + r16;
+        sc0[n] = FP8 ? a.s0[ch] : 1.0f;
+        sc1[n] = (FP8 && GATEUP) ? a.s1[ch] : 1.0f;
+    }
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
 #pragma unroll
@@ -273,19 +315,25 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
             for (int n = 0; n < NB; ++n) {
                 const int col = n0 + wn * WN_OUT + n * 16 + r16;
                 if constexpr (GATEUP) {
-                    const float g = acc[0][m][n][i];
-                    const float u = acc[1][m][n][i];
+                    float g = acc[0][m][n][i];
+                    float u = acc[1][m][n][i];
+                    if constexpr (FP8) {
+                        g = sc0[n] * g;
+                        u = sc1[n] * u;
+                    }
                     const float prod = (g * sigmoid_f32(g)) * u;
                     static_cast<uint16_t*>(a.out)[orow * a.N + col] = f32_to_bf16_rne(prod);
                 } else {
-                    static_cast<float*>(a.out)[orow * a.N + col] = acc[0][m][n][i];
+                    float v = acc[0][m][n][i];
+                    if constexpr (FP8) v = sc0[n] * v;
+                    static_cast<float*>(a.out)[orow * a.N + col] = v;
                 }
             }
         }
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP, bool FP8 = false>
 hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
     constexpr int BN_OUT = GATEUP ? BN / 2 : BN;
     const int64_t mtiles = (a.P + BM - 1) / BM + (a.E < a.P ? a.E : a.P);
@@ -293,7 +341,7 @@ hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
     const int64_t grid = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    ffn_gemm_kernel<BM, BN, WAVES_M, WAVES_N, GATEUP>
+    ffn_gemm_kernel<BM, BN, WAVES_M, WAVES_N, GATEUP, FP8>
         <<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
@@ -409,10 +457,10 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
     {
         const int64_t first = (static_cast<int64_t>(e) * a.N + n0) * K;
         const uint16_t* wbase;
-        if constexpr (GATEUP)
-            wbase = (wave < 2 ? a.b0 : a.b1) + first;  // waves 0-1: gate rows, 2-3: up rows
+        if constexpr (GATEUP)  // waves 0-1: gate rows, 2-3: up rows
+            wbase = static_cast<const uint16_t*>(wave < 2 ? a.b0 : a.b1) + first;
         else
-            wbase = a.b0 + first;
+            wbase = static_cast<const uint16_t*>(a.b0) + first;
         rsrc_b = make_rsrc(wbase, static_cast<uint32_t>((GATEUP ? BN_OUT : BN) * K * 2));
     }
 #pragma unroll
@@ -629,7 +677,8 @@ hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* so
                           const int32_t* offsets, const uint16_t* w_gate, const uint16_t* w_up,
                           uint16_t* h, hipStream_t s) {
     const int64_t P = p.T * p.k;
-    const FfnArgs a{P, p.T, p.k, p.E, p.H, p.I, x, sorted_pairs, offsets, w_gate, w_up, h};
+    const FfnArgs a{P, p.T, p.k, p.E, p.H, p.I, x, sorted_pairs, offsets, w_gate, w_up, h,
+                    nullptr, nullptr};
     const int64_t rows_per_expert = P / p.E;
     if (rows_per_expert <= 24) return launch_gemm<16, 128, 1, 4, true>(a, s);
     // the large-tile kernel addresses x with 32-bit buffer offsets
@@ -642,7 +691,8 @@ hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* so
 hipError_t launch_down(const Problem& p, const uint16_t* h, const int32_t* offsets,
                        const uint16_t* w_down, float* y, hipStream_t s) {
     const int64_t P = p.T * p.k;
-    const FfnArgs a{P, p.T, p.k, p.E, p.I, p.H, h, nullptr, offsets, w_down, nullptr, y};
+    const FfnArgs a{P, p.T, p.k, p.E, p.I, p.H, h, nullptr, offsets, w_down, nullptr, y, nullptr,
+                    nullptr};
     const int64_t rows_per_expert = P / p.E;
     if (rows_per_expert <= 24) return launch_gemm<16, 64, 1, 4, false>(a, s);
     if (rows_per_expert <= 96 || p.H % 256 != 0 || p.I % 128 != 0)
@@ -657,6 +707,24 @@ hipError_t launch_expert_ffn(const Problem& p, const uint16_t* x, const int32_t*
     const hipError_t err = launch_gate_up(p, x, sorted_pairs, offsets, w_gate, w_up, h, s);
     if (err != hipSuccess) return err;
     return launch_down(p, h, offsets, w_down, y, s);
+}
+
+hipError_t launch_expert_ffn_fp8(const Problem& p, const uint16_t* x, const int32_t* sorted_pairs,
+                                 const int32_t* offsets, const uint8_t* w_gate,
+                                 const float* s_gate, const uint8_t* w_up, const float* s_up,
+                                 const uint8_t* w_down, const float* s_down, uint16_t* h,
+                                 float* y, hipStream_t s) {
+    const int64_t P = p.T * p.k;
+    const int64_t rows_per_expert = P / p.E;
+    const FfnArgs gu{P, p.T, p.k, p.E, p.H, p.I, x, sorted_pairs, offsets, w_gate, w_up, h,
+                     s_gate, s_up};
+    hipError_t err = rows_per_expert <= 24 ? launch_gemm<16, 128, 1, 4, true, true>(gu, s)
+                                           : launch_gemm<64, 128, 1, 4, true, true>(gu, s);
+    if (err != hipSuccess) return err;
+    const FfnArgs dn{P, p.T, p.k, p.E, p.I, p.H, h, nullptr, offsets, w_down, nullptr, y, s_down,
+                     nullptr};
+    return rows_per_expert <= 24 ? launch_gemm<16, 64, 1, 4, false, true>(dn, s)
+                                 : launch_gemm<64, 128, 1, 4, false, true>(dn, s);
 }
 
 }  // namespace moe

@@ -36,6 +36,14 @@ hipError_t launch_expert_ffn(const Problem& p, const uint16_t* x, const int32_t*
                              const uint16_t* w_up, const uint16_t* w_down, uint16_t* h, float* y,
                              hipStream_t s);
 
+// The expert FFN with FP8 E4M3 weights and fp32 per-output-channel scales
+// (s_gate/s_up [E,I], s_down [E,H]); x, h and y as in launch_expert_ffn.
+hipError_t launch_expert_ffn_fp8(const Problem& p, const uint16_t* x, const int32_t* sorted_pairs,
+                                 const int32_t* offsets, const uint8_t* w_gate,
+                                 const float* s_gate, const uint8_t* w_up, const float* s_up,
+                                 const uint8_t* w_down, const float* s_down, uint16_t* h,
+                                 float* y, hipStream_t s);
+
 hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* sorted_pairs,
                           const int32_t* offsets, const uint16_t* w_gate, const uint16_t* w_up,
                           uint16_t* h, hipStream_t s);

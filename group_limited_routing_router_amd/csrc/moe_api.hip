@@ -278,6 +278,77 @@ MOE_EXPORT moe_status moe_dense_mlp(const moe_problem* p, const moe_bf16* x,
     return hip_status(e, "dense mlp launch");
 }
 
+MOE_EXPORT moe_status moe_expert_ffn_fp8(const moe_problem* p, const moe_bf16* x,
+                                         const int32_t* sorted_pairs,
+                                         const int32_t* expert_offsets, const uint8_t* w_gate,
+                                         const float* s_gate, const uint8_t* w_up,
+                                         const float* s_up, const uint8_t* w_down,
+                                         const float* s_down, float* y, void* ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+    MOE_TRY(check_problem(p));
+    if (p->T == 0) return ok();
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(sorted_pairs, "sorted_pairs"));
+    MOE_TRY(check_ptr(expert_offsets, "expert_offsets"));
+    MOE_TRY(check_ptr(w_gate, "w_gate"));
+    MOE_TRY(check_ptr(s_gate, "s_gate"));
+    MOE_TRY(check_ptr(w_up, "w_up"));
+    MOE_TRY(check_ptr(s_up, "s_up"));
+    MOE_TRY(check_ptr(w_down, "w_down"));
+    MOE_TRY(check_ptr(s_down, "s_down"));
+    MOE_TRY(check_ptr(y, "y"));
+    MOE_TRY(check_ws(*p, ws, ws_bytes));
+    const Layout L = layout_of(*p);
+    return hip_status(moe::launch_expert_ffn_fp8(to_internal(*p), x, sorted_pairs, expert_offsets,
+                                                 w_gate, s_gate, w_up, s_up, w_down, s_down,
+                                                 at<uint16_t>(ws, L.h), y, stream),
+                      "fp8 expert ffn launch");
+}
+
+MOE_EXPORT moe_status moe_forward_fp8(const moe_problem* p, const moe_bf16* x,
+                                      const moe_bf16* w_router, const float* bias,
+                                      const uint8_t* w_gate, const float* s_gate,
+                                      const uint8_t* w_up, const float* s_up,
+                                      const uint8_t* w_down, const float* s_down, void* out,
+                                      moe_dtype out_dtype, int32_t* topk_ids,
+                                      float* topk_weights, float* y, void* ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+    MOE_TRY(check_problem(p));
+    if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16)
+        return fail(MOE_ERR_INVALID_ARG, "out_dtype=%d is not MOE_DTYPE_F32/BF16", (int)out_dtype);
+    if (p->T == 0) return ok();
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(w_router, "w_router"));
+    MOE_TRY(check_ptr(bias, "bias", true));
+    MOE_TRY(check_ptr(w_gate, "w_gate"));
+    MOE_TRY(check_ptr(s_gate, "s_gate"));
+    MOE_TRY(check_ptr(w_up, "w_up"));
+    MOE_TRY(check_ptr(s_up, "s_up"));
+    MOE_TRY(check_ptr(w_down, "w_down"));
+    MOE_TRY(check_ptr(s_down, "s_down"));
+    MOE_TRY(check_ptr(out, "out"));
+    MOE_TRY(check_ptr(topk_ids, "topk_ids", true));
+    MOE_TRY(check_ptr(topk_weights, "topk_weights", true));
+    MOE_TRY(check_ptr(y, "y"));
+    MOE_TRY(check_ws(*p, ws, ws_bytes));
+    const Layout L = layout_of(*p);
+    const moe::Problem q = to_internal(*p);
+    int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, L.ids);
+    float* wts = topk_weights ? topk_weights : at<float>(ws, L.weights);
+    int32_t* off = at<int32_t>(ws, L.offsets);
+    int32_t* sorted = at<int32_t>(ws, L.sorted);
+    int32_t* rows = at<int32_t>(ws, L.rows);
+    hipError_t e = moe::launch_route(q, x, w_router, bias, ids, wts, stream);
+    if (e != hipSuccess) return hip_status(e, "route launch");
+    e = moe::launch_permute(q, ids, off, sorted, rows, at<int32_t>(ws, L.counts), stream);
+    if (e != hipSuccess) return hip_status(e, "permute launch");
+    e = moe::launch_expert_ffn_fp8(q, x, sorted, off, w_gate, s_gate, w_up, s_up, w_down, s_down,
+                                   at<uint16_t>(ws, L.h), y, stream);
+    if (e != hipSuccess) return hip_status(e, "fp8 expert ffn launch");
+    e = moe::launch_combine(q, y, rows, wts, out, out_dtype == MOE_DTYPE_BF16, stream);
+    return hip_status(e, "combine launch");
+}
+
 MOE_EXPORT moe_status moe_forward(const moe_problem* p, const moe_bf16* x,
                                   const moe_bf16* w_router, const float* bias,
                                   const moe_bf16* w_gate, const moe_bf16* w_up,

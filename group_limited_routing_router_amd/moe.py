@@ -50,7 +50,8 @@ class MoEProblem(ctypes.Structure):
 
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
            "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_combine_residual",
-           "moe_dense_mlp", "moe_forward", "moe_status_string", "moe_last_error")
+           "moe_dense_mlp", "moe_expert_ffn_fp8", "moe_forward", "moe_forward_fp8",
+           "moe_status_string", "moe_last_error")
 
 
 def library_path() -> str:
@@ -103,6 +104,12 @@ def load_library():
         lib.moe_combine_residual.argtypes = [prob, P, P, P, P, ctypes.c_float, ctypes.c_int32, P,
                                              P]
         lib.moe_combine_residual.restype = st
+        lib.moe_expert_ffn_fp8.argtypes = [prob, P, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t,
+                                           P]
+        lib.moe_expert_ffn_fp8.restype = st
+        lib.moe_forward_fp8.argtypes = [prob, P, P, P, P, P, P, P, P, P, P, ctypes.c_int, P, P, P,
+                                        P, ctypes.c_size_t, P]
+        lib.moe_forward_fp8.restype = st
         lib.moe_dense_mlp.argtypes = [prob, P, P, P, P, P, P, ctypes.c_size_t, P]
         lib.moe_dense_mlp.restype = st
         lib.moe_forward.argtypes = [prob, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, P,
@@ -191,6 +198,25 @@ def moe_combine_residual(p, y, pair_rows, topk_weights, norm_weight, eps, step, 
     _check(load_library().moe_combine_residual(ctypes.byref(p), _p(y), _p(pair_rows),
                                                 _p(topk_weights), _p(norm_weight), float(eps),
                                                 int(step), _p(residual), _stream(stream)))
+
+
+def moe_expert_ffn_fp8(p, x, sorted_pairs, expert_offsets, q_gate, s_gate, q_up, s_up, q_down,
+                       s_down, y, ws, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().moe_expert_ffn_fp8(ctypes.byref(p), _p(x), _p(sorted_pairs),
+                                              _p(expert_offsets), _p(q_gate), _p(s_gate), _p(q_up),
+                                              _p(s_up), _p(q_down), _p(s_down), _p(y), _p(ws),
+                                              nbytes, _stream(stream)))
+
+
+def moe_forward_fp8(p, x, w_router, bias, q_gate, s_gate, q_up, s_up, q_down, s_down, out,
+                    topk_ids, topk_weights, y, ws, stream=None):
+    nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+    _check(load_library().moe_forward_fp8(ctypes.byref(p), _p(x), _p(w_router), _p(bias),
+                                           _p(q_gate), _p(s_gate), _p(q_up), _p(s_up), _p(q_down),
+                                           _p(s_down), _p(out), _dtype_code(out), _p(topk_ids),
+                                           _p(topk_weights), _p(y), _p(ws), nbytes,
+                                           _stream(stream)))
 
 
 def moe_dense_mlp(p, x, w_gate, w_up, w_down, out, ws, stream=None):

@@ -180,6 +180,32 @@ moe_status moe_dense_mlp(const moe_problem* p, const moe_bf16* x, const moe_bf16
                          const moe_bf16* w_up, const moe_bf16* w_down, float* out, void* ws,
                          size_t ws_bytes, hipStream_t stream);
 
+/* FP8 expert weights.  The pages give no FP8 scheme for the experts; the one
+ * taken: every weight matrix is stored as FP8 E4M3 codes (the OCP e4m3fn
+ * encoding: bias 7, no infinities, 0x7f/0xff NaN) with one fp32 scale per
+ * output channel, and a channel's dot product is its scale times the dot
+ * product with the decoded codes:
+ *   g[n] = s_gate[e,n] * (x_q . w_gate[e,n]),  u[n] = s_up[e,n] * (x_q . w_up[e,n])
+ *   h[n] = bf16(silu(g[n]) * u[n]),            y[m] = s_down[e,m] * (h . w_down[e,m])
+ * Activations, h, y and every accumulation are as in the bf16 calls; the codes
+ * are widened to bf16 exactly and multiplied on the bf16 MFMA path.  Halves
+ * the bytes of the weight stream.
+ *   w_gate, w_up  [E,I,H] uint8 codes;  s_gate, s_up  [E,I] fp32
+ *   w_down        [E,H,I] uint8 codes;  s_down        [E,H] fp32
+ * Everything else as moe_expert_ffn / moe_forward. */
+moe_status moe_expert_ffn_fp8(const moe_problem* p, const moe_bf16* x,
+                              const int32_t* sorted_pairs, const int32_t* expert_offsets,
+                              const uint8_t* w_gate, const float* s_gate, const uint8_t* w_up,
+                              const float* s_up, const uint8_t* w_down, const float* s_down,
+                              float* y, void* ws, size_t ws_bytes, hipStream_t stream);
+
+moe_status moe_forward_fp8(const moe_problem* p, const moe_bf16* x, const moe_bf16* w_router,
+                           const float* bias, const uint8_t* w_gate, const float* s_gate,
+                           const uint8_t* w_up, const float* s_up, const uint8_t* w_down,
+                           const float* s_down, void* out, moe_dtype out_dtype,
+                           int32_t* topk_ids, float* topk_weights, float* y, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
 /* The whole block: route, permute, expert FFN, combine.
  *   topk_ids, topk_weights  optional [T,k] outputs (NULL: kept in `ws`)
  *   y                       [T*k,H] fp32 caller buffer for expert outputs
