@@ -136,20 +136,16 @@ __device__ bool find_tile(const FfnArgs& a, int ncol_tiles, int32_t* s_off, int3
     return true;
 }
 
-// FP8 E4M3 codes -> bf16, eight at a time: the hardware conversion to fp32 is
-// exact (and follows the OCP e4m3fn encoding on gfx950) and every E4M3 value
-// is a bf16 value, so the upper half of each fp32 is the bf16.
+// FP8 E4M3 codes -> bf16, eight at a time, two per instruction.  With a unit
+// scale the gfx950 conversion is exact (OCP e4m3fn codes; every E4M3 value is
+// a bf16 value) and NaN codes stay NaN.
 __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     u32x4 r;
-    const uint32_t w[2] = {lo, hi};
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const f32x2 a = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], false);
-        const f32x2 b = __builtin_amdgcn_cvt_pk_f32_fp8(w[i], true);
-        r[2 * i] = __builtin_amdgcn_perm(__float_as_uint(a[1]), __float_as_uint(a[0]), 0x07060302u);
-        r[2 * i + 1] = __builtin_amdgcn_perm(__float_as_uint(b[1]), __float_as_uint(b[0]), 0x07060302u);
-    }
+    r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+    r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+    r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+    r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
     return as_bf16x8(r);
 }
 
@@ -409,7 +405,11 @@ __device__ __forceinline__ void quad_transpose(float& v0, float& v1, float& v2, 
     v3 = b0 ? n3 : y;
 }
 
-template <bool GATEUP>
+// FP8 = true: the weights are E4M3 codes (64 bytes a row and stage, 16 rows
+// per 1-KB load, 16-byte chunk c of row r at c ^ ((r >> 2) & 3)), widened to
+// bf16 as each MFMA operand is read; the per-channel scale multiplies the
+// accumulators before the results are stored.
+template <bool GATEUP, bool FP8 = false>
 __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
     constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 2;
     constexpr int BN_OUT = GATEUP ? BN / 2 : BN;
@@ -418,14 +418,20 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
     constexpr int NB = WN_OUT / 32;
     constexpr int NACC = GATEUP ? 2 : 1;
     constexpr int NFB = NACC * NB;             // B fragments per substep (4)
-    constexpr int ROW_BYTES = BK * 2;          // 128
+    constexpr int ROW_BYTES = BK * 2;          // 128 (activations)
+    constexpr int EB = FP8 ? 1 : 2;            // bytes per weight
+    constexpr int B_ROW = BK * EB;             // 128 or 64 (weights)
     constexpr int A_STAGE = BM * ROW_BYTES;    // 32 KB
-    constexpr int B_STAGE = BN * ROW_BYTES;    // 32 KB
+    constexpr int B_STAGE = BN * B_ROW;        // 32 or 16 KB
     constexpr int A_BUFS = 2, B_BUFS = 3;
-    static_assert(A_BUFS * A_STAGE + B_BUFS * B_STAGE == kDmaArena, "LDS budget");
-    constexpr int DMA_PER_WAVE = BM / kWaves / 8;  // 1-KB loads per wave per operand (8)
+    constexpr int ARENA = A_BUFS * A_STAGE + B_BUFS * B_STAGE;
+    static_assert(ARENA <= kDmaArena, "LDS budget");
+    constexpr int DMA_A = BM / kWaves / 8;     // 1-KB activation loads per wave and stage (8)
+    constexpr int B_RPL = 1024 / B_ROW;        // weight rows per 1-KB load (8 or 16)
+    constexpr int B_LPR = B_ROW / 16;          // lanes per weight row (8 or 4)
+    constexpr int DMA_B = BN / kWaves / B_RPL; // weight loads per wave and stage (8 or 4)
 
-    __shared__ __attribute__((aligned(1024))) unsigned char s_arena[kDmaArena];
+    __shared__ __attribute__((aligned(1024))) unsigned char s_arena[ARENA];
     const uint32_t arena = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_arena));
 
     const int tid = threadIdx.x;
@@ -448,23 +454,23 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
     // chunk L % 8, i.e. logical chunk (L % 8) ^ ((row >> 1) & 7). ----
     constexpr uint32_t kOutside = 0x80000000u;
     __amdgpu_buffer_rsrc_t rsrc_a, rsrc_b;
-    uint32_t va[DMA_PER_WAVE], vb[DMA_PER_WAVE];
+    uint32_t va[DMA_A], vb[DMA_B];
     if constexpr (GATEUP)
         rsrc_a = make_rsrc(a.a_src, static_cast<uint32_t>(a.T * K * 2));
     else
         rsrc_a = make_rsrc(a.a_src + static_cast<int64_t>(row0) * K,
                            static_cast<uint32_t>(rows * K * 2));
     {
-        const int64_t first = (static_cast<int64_t>(e) * a.N + n0) * K;
-        const uint16_t* wbase;
+        const int64_t first = (static_cast<int64_t>(e) * a.N + n0) * K * EB;
+        const unsigned char* wbase;
         if constexpr (GATEUP)  // waves 0-1: gate rows, 2-3: up rows
-            wbase = static_cast<const uint16_t*>(wave < 2 ? a.b0 : a.b1) + first;
+            wbase = static_cast<const unsigned char*>(wave < 2 ? a.b0 : a.b1) + first;
         else
-            wbase = static_cast<const uint16_t*>(a.b0) + first;
-        rsrc_b = make_rsrc(wbase, static_cast<uint32_t>((GATEUP ? BN_OUT : BN) * K * 2));
+            wbase = static_cast<const unsigned char*>(a.b0) + first;
+        rsrc_b = make_rsrc(wbase, static_cast<uint32_t>((GATEUP ? BN_OUT : BN) * K * EB));
     }
 #pragma unroll
-    for (int j = 0; j < DMA_PER_WAVE; ++j) {
+    for (int j = 0; j < DMA_A; ++j) {
         const int r = wave * 64 + j * 8 + (lane >> 3);
         const int c = (lane & 7) ^ ((r >> 1) & 7);
         uint32_t av;
@@ -479,8 +485,13 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
             av = static_cast<uint32_t>(r * K * 2 + c * 16);
         }
         va[j] = av;
+    }
+#pragma unroll
+    for (int j = 0; j < DMA_B; ++j) {
+        const int r = wave * 64 + j * B_RPL + lane / B_LPR;
+        const int c = FP8 ? ((lane % B_LPR) ^ ((r >> 2) & 3)) : ((lane % B_LPR) ^ ((r >> 1) & 7));
         const int rb = GATEUP ? (r & (BN_OUT - 1)) : r;  // row within the gate / up half
-        vb[j] = static_cast<uint32_t>(rb * K * 2 + c * 16);
+        vb[j] = static_cast<uint32_t>(rb * K * EB + c * 16);
     }
     auto a_buf = [&](int i) { return arena + i * A_STAGE; };
     auto b_buf = [&](int i) { return arena + A_BUFS * A_STAGE + i * B_STAGE; };
@@ -489,8 +500,8 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
                    static_cast<uint32_t>(kt * ROW_BYTES));
     };
     auto dma_b = [&](int j, int buf, int kt) {
-        dma_load16(b_buf(buf) + (wave * 64 + j * 8) * ROW_BYTES, rsrc_b, vb[j],
-                   static_cast<uint32_t>(kt * ROW_BYTES));
+        dma_load16(b_buf(buf) + (wave * 64 + j * B_RPL) * B_ROW, rsrc_b, vb[j],
+                   static_cast<uint32_t>(kt * B_ROW));
     };
 
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -532,9 +543,18 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
 #pragma unroll
                 for (int g = 0; g < NACC; ++g)
 #pragma unroll
-                    for (int n = 0; n < NB; ++n)
-                        f.b[g * NB + n] = *reinterpret_cast<const bf16x8*>(
-                            sb + frag_off(g * BN_OUT + wn * WN_OUT + n * 32 + r32, c));
+                    for (int n = 0; n < NB; ++n) {
+                        const int br = g * BN_OUT + wn * WN_OUT + n * 32 + r32;
+                        if constexpr (FP8) {
+                            // 8 codes: 8-byte half (c & 1) of chunk (c >> 1)
+                            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                            const u32x2 w8 = *reinterpret_cast<const u32x2*>(
+                                sb + br * B_ROW + ((((c >> 1) ^ ((br >> 2) & 3))) << 4) + ((c & 1) << 3));
+                            f.b[g * NB + n] = e4m3x8_to_bf16x8(w8[0], w8[1]);
+                        } else {
+                            f.b[g * NB + n] = *reinterpret_cast<const bf16x8*>(sb + frag_off(br, c));
+                        }
+                    }
             }
         };
         auto mfma_one = [&](const Frags& f, auto ic) {
@@ -550,12 +570,12 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
         const int nk = K / BK;
         // prologue: A(0), B(0), B(1) in flight; wait for the first two
 #pragma unroll
-        for (int j = 0; j < DMA_PER_WAVE; ++j) dma_a(j, 0, 0);
+        for (int j = 0; j < DMA_A; ++j) dma_a(j, 0, 0);
 #pragma unroll
-        for (int j = 0; j < DMA_PER_WAVE; ++j) dma_b(j, 0, 0);
+        for (int j = 0; j < DMA_B; ++j) dma_b(j, 0, 0);
 #pragma unroll
-        for (int j = 0; j < DMA_PER_WAVE; ++j) dma_b(j, 1, nk > 1 ? 1 : 0);
-        wait_vmcnt<DMA_PER_WAVE>();
+        for (int j = 0; j < DMA_B; ++j) dma_b(j, 1, nk > 1 ? 1 : 0);
+        wait_vmcnt<DMA_B>();
         __syncthreads();
         int abuf = 0, bbuf = 0;
         for (int kt = 0; kt < nk; ++kt) {
@@ -573,7 +593,8 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
             load_frags(f0, abuf, bbuf, 0);
             load_frags(f1, abuf, bbuf, 1);
             __builtin_amdgcn_sched_barrier(0);
-            constexpr int LPS = 2 * DMA_PER_WAVE / 4;  // loads per substep (4)
+            constexpr int LPS = (DMA_A + DMA_B) / 4;  // loads per substep (4, FP8: 3)
+            static_assert(LPS * 4 == DMA_A + DMA_B, "loads split evenly over the substeps");
             auto substep = [&](const Frags& f, auto sc) {
                 constexpr int sub = decltype(sc)::value;
                 static_for<0, (MF > LPS ? MF : LPS)>([&](auto ic) {
@@ -583,10 +604,10 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
                     constexpr int step = MF >= LPS ? MF / LPS : 1;
                     if constexpr (i % step == step - 1 && i / step < LPS) {
                         constexpr int j = sub * LPS + i / step;
-                        if constexpr (j < DMA_PER_WAVE)
+                        if constexpr (j < DMA_A)
                             dma_a(j, anext, ka);
                         else
-                            dma_b(j - DMA_PER_WAVE, bnext, kb);
+                            dma_b(j - DMA_A, bnext, kb);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 });
@@ -600,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
             substep(f0, std::integral_constant<int, 2>{});
             substep(f1, std::integral_constant<int, 3>{});
             // A(kt+1) and B(kt+1) have landed once only B(kt+2) is outstanding
-            wait_vmcnt<DMA_PER_WAVE>();
+            wait_vmcnt<DMA_B>();
             __syncthreads();
             abuf = anext;
             bbuf = bbuf == 2 ? 0 : bbuf + 1;
@@ -623,6 +644,22 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
         // contiguous outputs and one store instruction covers 8 rows x 32
         // columns.
         const int t = lane & 3, q4 = (lane & 31) >> 2;
+        if constexpr (FP8) {
+            // per-channel scales: this lane's column of each accumulator block
+#pragma unroll
+            for (int n = 0; n < NB; ++n) {
+                const int64_t ch = static_cast<int64_t>(e) * a.N + n0 + wn * WN_OUT + n * 32 + r32;
+                const float s0 = a.s0[ch];
+                const float s1 = GATEUP ? a.s1[ch] : 1.0f;
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        acc[0][m][n][i] = s0 * acc[0][m][n][i];
+                        if constexpr (GATEUP) acc[1][m][n][i] = s1 * acc[1][m][n][i];
+                    }
+            }
+        }
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
             if (m >= mb_valid) continue;
@@ -659,7 +696,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
     }
 }
 
-template <bool GATEUP>
+template <bool GATEUP, bool FP8 = false>
 hipError_t launch_gemm_dma(const FfnArgs& a, hipStream_t s) {
     constexpr int BM = 256, BN_OUT = GATEUP ? 128 : 256;
     const int64_t mtiles = (a.P + BM - 1) / BM + (a.E < a.P ? a.E : a.P);
@@ -667,7 +704,7 @@ hipError_t launch_gemm_dma(const FfnArgs& a, hipStream_t s) {
     const int64_t grid = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    ffn_gemm_dma_kernel<GATEUP><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s>>>(a);
+    ffn_gemm_dma_kernel<GATEUP, FP8><<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -718,13 +755,23 @@ hipError_t launch_expert_ffn_fp8(const Problem& p, const uint16_t* x, const int3
     const int64_t rows_per_expert = P / p.E;
     const FfnArgs gu{P, p.T, p.k, p.E, p.H, p.I, x, sorted_pairs, offsets, w_gate, w_up, h,
                      s_gate, s_up};
-    hipError_t err = rows_per_expert <= 24 ? launch_gemm<16, 128, 1, 4, true, true>(gu, s)
-                                           : launch_gemm<64, 128, 1, 4, true, true>(gu, s);
+    // few rows per expert: the weight stream is the cost, so a tile takes
+    // twice the weight rows of the bf16 kernels (the same bytes per stage)
+    const bool x_fits = p.T * static_cast<int64_t>(p.H) * 2 < (static_cast<int64_t>(1) << 31);
+    hipError_t err;
+    if (rows_per_expert <= 24 && p.I % 128 == 0)
+        err = launch_gemm<16, 256, 1, 4, true, true>(gu, s);
+    else if (rows_per_expert <= 96 || p.I % 128 != 0 || !x_fits)
+        err = launch_gemm<64, 128, 1, 4, true, true>(gu, s);
+    else
+        err = launch_gemm_dma<true, true>(gu, s);
     if (err != hipSuccess) return err;
     const FfnArgs dn{P, p.T, p.k, p.E, p.I, p.H, h, nullptr, offsets, w_down, nullptr, y, s_down,
                      nullptr};
-    return rows_per_expert <= 24 ? launch_gemm<16, 64, 1, 4, false, true>(dn, s)
-                                 : launch_gemm<64, 128, 1, 4, false, true>(dn, s);
+    if (rows_per_expert <= 24 && p.H % 128 == 0) return launch_gemm<16, 128, 1, 4, false, true>(dn, s);
+    if (rows_per_expert <= 96 || p.H % 256 != 0 || p.I % 128 != 0)
+        return launch_gemm<64, 128, 1, 4, false, true>(dn, s);
+    return launch_gemm_dma<false, true>(dn, s);
 }
 
 }  // namespace moe

@@ -2,9 +2,10 @@
 moe_expert_ffn_fp8) against the oracle's FP8 expert (ffn_pairs_fp8) on the
 GPU's own routing.
 
-Small shapes are compared on every output; the Beam decode shape on seeded
-sampled (token, slot) pairs the oracle computes one by one.  Shapes reach the
-16-row and 64-row tiles, ragged row tails and several column tiles."""
+Small shapes are compared on every output; the Beam decode and prefill
+shapes on seeded sampled (token, slot) pairs the oracle computes one by one.
+Shapes reach the 16-row, 64-row and large tiles, ragged row tails and several
+column tiles."""
 import numpy as np
 import pytest
 import torch
@@ -45,8 +46,9 @@ def _run(moe, cfg, d, w):
 SMALL = [
     # (T, H, I, E, G, TG, k)
     (64, 256, 128, 16, 4, 2, 4),      # ~16 rows per expert: 16-row tiles
-    (600, 512, 256, 16, 4, 2, 4),     # ~150 rows per expert: 64-row tiles, ragged tails
+    (600, 512, 256, 16, 4, 2, 4),     # ~150 rows per expert: large tiles, ragged tails
     (33, 384, 192, 32, 4, 2, 6),
+    (300, 256, 192, 8, 2, 1, 2),      # ~75 rows per expert: 64-row tiles
 ]
 
 
@@ -77,11 +79,17 @@ def test_fp8_small(moe, shape):
     assert ey <= OUT_TOL and eo <= OUT_TOL
 
 
-def test_fp8_beam_decode_sampled(moe):
-    cfg = CONFIGS["decode"]
-    print(f"[case] fp8 beam decode T={cfg.T}", flush=True)
+@pytest.fixture(scope="module")
+def beam_fp8():
+    return make_weights_fp8(CONFIGS["decode"], seed=0, device="cuda")
+
+
+@pytest.mark.parametrize("name", ["decode", "prefill"])
+def test_fp8_beam_sampled(moe, beam_fp8, name):
+    cfg = CONFIGS[name]
+    print(f"[case] fp8 beam {name} T={cfg.T}", flush=True)
     d = make_tokens(cfg, seed=0, device="cuda")
-    w = make_weights_fp8(cfg, seed=0, device="cuda")
+    w = beam_fp8
     b = _run(moe, cfg, d, w)
     ids = b["topk_ids"].cpu().numpy()
     sp = b["sorted_pairs"].cpu().numpy()
