@@ -33,8 +33,10 @@ if ROOT not in sys.path:
 PEAK_BF16 = 2.5166e15   # dense bf16 MFMA, FLOP/s (MI355X published)
 PEAK_HBM = 8.0e12       # HBM3E, B/s (MI355X published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = ["group_limited_routing_router_amd/csrc/ffn.hip",
-                  "group_limited_routing_router_amd/csrc/common.h"]
+KERNEL_SOURCES = sorted(
+    os.path.join("group_limited_routing_router_amd", "csrc", f)
+    for f in os.listdir(os.path.join(ROOT, "group_limited_routing_router_amd", "csrc"))
+    if f.endswith((".hip", ".h")))
 
 
 def log(*a):
