@@ -77,11 +77,14 @@ struct FfnArgs {
 // Map this workgroup to a tile (expert e, column tile nt, row range
 // [row0, row0 + rows)).  Every workgroup rebuilds the prefix sum of per-expert
 // row tiles from expert_offsets in LDS (no host read-back); an expert with n
-// rows gets ceil(n / BM) row tiles of balanced size.  Workgroup b runs on XCD
-// b % 8; XCD x takes the x-th contiguous run of the tile list, ordered expert,
-// then column tile, then row tile, so the row tiles that share a weight tile
-// are neighbours on one XCD.  Returns false for surplus workgroups (uniform
-// over the workgroup).
+// rows gets ceil(n / BM) row tiles of balanced size.  The tile list is ordered
+// by expert position, then column tile, then row tile; workgroup b runs on
+// XCD b % 8 and XCD x takes the x-th contiguous run of the list, so the row
+// tiles that share a weight tile are neighbours on one XCD.  Expert positions
+// interleave the experts (position i holds expert (i % 8) * (E / 8) + i / 8
+// when 8 divides E), so each XCD's run draws on every group of consecutive
+// experts and a few heavily routed neighbours do not land on one XCD.
+// Returns false for surplus workgroups (uniform over the workgroup).
 template <int BM>
 __device__ bool find_tile(const FfnArgs& a, int ncol_tiles, int32_t* s_off, int32_t* s_tstart,
                           int& e_out, int& nt_out, int& row0_out, int& rows_out) {
@@ -93,9 +96,13 @@ __device__ bool find_tile(const FfnArgs& a, int ncol_tiles, int32_t* s_off, int3
         s_off[e] = static_cast<int32_t>(o);
     }
     __syncthreads();
+    // expert at list position i
+    const bool interleave = E % kNumXcd == 0;
+    auto expert_at = [&](int i) { return interleave ? (i % kNumXcd) * (E / kNumXcd) + i / kNumXcd : i; };
     int cnt = 0;
     if (tid < E) {
-        const int n = s_off[tid + 1] - s_off[tid];
+        const int ex = expert_at(tid);
+        const int n = s_off[ex + 1] - s_off[ex];
         cnt = n > 0 ? (n + BM - 1) / BM : 0;
     }
     s_tstart[tid] = cnt;  // kThreads == kMaxE
@@ -108,7 +115,7 @@ __device__ bool find_tile(const FfnArgs& a, int ncol_tiles, int32_t* s_off, int3
     }
     const int incl = s_tstart[tid];
     __syncthreads();
-    s_tstart[tid + 1] = incl;  // exclusive prefix; s_tstart[E] = total row tiles
+    s_tstart[tid + 1] = incl;  // exclusive prefix over positions; s_tstart[E] = total row tiles
     if (tid == 0) s_tstart[0] = 0;
     __syncthreads();
     const int64_t total = static_cast<int64_t>(s_tstart[E]) * ncol_tiles;
@@ -117,14 +124,15 @@ __device__ bool find_tile(const FfnArgs& a, int ncol_tiles, int32_t* s_off, int3
     const int64_t per = total / kNumXcd, rem = total % kNumXcd;
     if (local >= per + (xcd < rem ? 1 : 0)) return false;
     const int64_t L = xcd * per + (xcd < rem ? xcd : rem) + local;
-    int lo = 0, hi = E - 1;  // last e with s_tstart[e] * ncol_tiles <= L
+    int lo = 0, hi = E - 1;  // last position i with s_tstart[i] * ncol_tiles <= L
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
         if (static_cast<int64_t>(s_tstart[mid]) * ncol_tiles <= L) lo = mid; else hi = mid - 1;
     }
-    const int e = lo;
-    const int tiles_e = s_tstart[e + 1] - s_tstart[e];  // >= 1 for the expert found
-    const int64_t rel = L - static_cast<int64_t>(s_tstart[e]) * ncol_tiles;
+    const int pos = lo;
+    const int e = expert_at(pos);
+    const int tiles_e = s_tstart[pos + 1] - s_tstart[pos];  // >= 1 for the position found
+    const int64_t rel = L - static_cast<int64_t>(s_tstart[pos]) * ncol_tiles;
     const int nt = static_cast<int>(rel / tiles_e);
     const int mt = static_cast<int>(rel - static_cast<int64_t>(nt) * tiles_e);
     const int n_e = s_off[e + 1] - s_off[e];
