@@ -77,15 +77,19 @@ struct FfnArgs {
 // Map this workgroup to a tile (expert e, column tile nt, row range
 // [row0, row0 + rows)).  Every workgroup rebuilds the prefix sum of per-expert
 // row tiles from expert_offsets in LDS (no host read-back); an expert with n
-// rows gets ceil(n / BM) row tiles of balanced size.  The tile list is ordered
+// rows gets ceil(n / BM) row tiles.  The tile list is ordered
 // by expert position, then column tile, then row tile; workgroup b runs on
 // XCD b % 8 and XCD x takes the x-th contiguous run of the list, so the row
 // tiles that share a weight tile are neighbours on one XCD.  Expert positions
 // interleave the experts (position i holds expert (i % 8) * (E / 8) + i / 8
 // when 8 divides E), so each XCD's run draws on every group of consecutive
 // experts and a few heavily routed neighbours do not land on one XCD.
-// Returns false for surplus workgroups (uniform over the workgroup).
-template <int BM>
+// GRAN = 1 splits an expert's rows evenly over its row tiles; GRAN > 1 gives
+// every row tile but the last the same multiple of GRAN rows (for the large
+// tile, whose two row waves take alternate 32-row blocks: 64-row multiples
+// keep them equally busy).  Returns false for surplus workgroups (uniform
+// over the workgroup).
+template <int BM, int GRAN = 1>
 __device__ bool find_tile(const FfnArgs& a, int ncol_tiles, int32_t* s_off, int32_t* s_tstart,
                           int& e_out, int& nt_out, int& row0_out, int& rows_out) {
     const int tid = threadIdx.x;
@@ -136,11 +140,19 @@ __device__ bool find_tile(const FfnArgs& a, int ncol_tiles, int32_t* s_off, int3
     const int nt = static_cast<int>(rel / tiles_e);
     const int mt = static_cast<int>(rel - static_cast<int64_t>(nt) * tiles_e);
     const int n_e = s_off[e + 1] - s_off[e];
-    const int base = n_e / tiles_e, extra = n_e % tiles_e;
     e_out = e;
     nt_out = nt;
-    row0_out = s_off[e] + mt * base + (mt < extra ? mt : extra);
-    rows_out = base + (mt < extra ? 1 : 0);
+    if constexpr (GRAN == 1) {
+        const int base = n_e / tiles_e, extra = n_e % tiles_e;
+        row0_out = s_off[e] + mt * base + (mt < extra ? mt : extra);
+        rows_out = base + (mt < extra ? 1 : 0);
+    } else {
+        // per <= BM since GRAN divides BM, so the last tile keeps >= 1 row
+        static_assert(BM % GRAN == 0, "granule divides the tile");
+        const int per = ((n_e + tiles_e - 1) / tiles_e + GRAN - 1) / GRAN * GRAN;
+        row0_out = s_off[e] + mt * per;
+        rows_out = min(per, n_e - mt * per);
+    }
     return true;
 }
 
@@ -389,30 +401,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// Lanes of a quad exchange values so that a 4 x 4 block held one column per
-// lane (v[r] = row r) ends up one row per lane (v[c] = column c): two
-// butterfly stages, each one quad permute (DPP) and selects per value pair.
-__device__ __forceinline__ float dpp_xor1(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, true));
-}
-__device__ __forceinline__ float dpp_xor2(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, true));
-}
-__device__ __forceinline__ void quad_transpose(float& v0, float& v1, float& v2, float& v3) {
-    const int t = threadIdx.x & 3;
-    const bool b1 = (t & 2) != 0, b0 = (t & 1) != 0;
-    float y = dpp_xor2(b1 ? v0 : v2);  // rows 0/2 across lane bit 1
-    float n0 = b1 ? y : v0, n2 = b1 ? v2 : y;
-    y = dpp_xor2(b1 ? v1 : v3);
-    float n1 = b1 ? y : v1, n3 = b1 ? v3 : y;
-    y = dpp_xor1(b0 ? n0 : n1);        // rows 0/1 and 2/3 across lane bit 0
-    v0 = b0 ? y : n0;
-    v1 = b0 ? n1 : y;
-    y = dpp_xor1(b0 ? n2 : n3);
-    v2 = b0 ? y : n2;
-    v3 = b0 ? n3 : y;
-}
-
 // FP8 = true: the weights are E4M3 codes (64 bytes a row and stage, 16 rows
 // per 1-KB load, 16-byte chunk c of row r at c ^ ((r >> 2) & 3)), widened to
 // bf16 as each MFMA operand is read; the per-channel scale multiplies the
@@ -450,7 +438,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
     {
         int32_t* s_off = reinterpret_cast<int32_t*>(s_arena);
         int32_t* s_tstart = s_off + (kMaxE + 1);
-        if (!find_tile<BM>(a, a.N / BN_OUT, s_off, s_tstart, e, nt, row0, rows)) return;
+        if (!find_tile<BM, 32 * WAVES_M>(a, a.N / BN_OUT, s_off, s_tstart, e, nt, row0, rows)) return;
         __syncthreads();  // everyone is done with the schedule before DMA reuses the arena
     }
     const int n0 = nt * BN_OUT;
@@ -586,6 +574,8 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
         wait_vmcnt<DMA_B>();
         __syncthreads();
         int abuf = 0, bbuf = 0;
+        Frags f0, f1;
+        load_frags(f0, 0, 0, 0);
         for (int kt = 0; kt < nk; ++kt) {
             const int ka = kt + 1 < nk ? kt + 1 : nk - 1;   // past the end: refill an idle buffer
             const int kb = kt + 2 < nk ? kt + 2 : nk - 1;
@@ -594,23 +584,31 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
             // Phases are pinned with scheduling fences (the compiler would
             // otherwise sink fragment reads next to their MFMAs): fragment
             // reads of a substep are issued one substep ahead, and the
-            // stage's 16 loads are spread evenly over its MFMAs (activations
-            // first, they are needed one stage ahead; weights after), so the
-            // texture unit never backs up into the MFMA issue stream.
-            Frags f0, f1;
-            load_frags(f0, abuf, bbuf, 0);
+            // stage's loads are spread evenly over its MFMAs up to the stage
+            // barrier (activations first, they are needed one stage ahead;
+            // weights after), so the texture unit never backs up into the
+            // MFMA issue stream.  The stage barrier sits before the last
+            // eighth of the last substep's MFMAs: the first fragments of the
+            // next stage are read while those run, so the matrix pipe does
+            // not wait out a whole LDS round trip at every stage (a later
+            // barrier leaves the loads of the next stage more time to land).
             load_frags(f1, abuf, bbuf, 1);
             __builtin_amdgcn_sched_barrier(0);
             constexpr int LPS = (DMA_A + DMA_B) / 4;  // loads per substep (4, FP8: 3)
             static_assert(LPS * 4 == DMA_A + DMA_B, "loads split evenly over the substeps");
-            auto substep = [&](const Frags& f, auto sc) {
+            // MFMAs [LO, HI) of substep SUB; a negative SUB issues no loads,
+            // else that substep's loads are spread over these MFMAs
+            auto substep = [&](const Frags& f, auto sc, auto lo_c, auto hi_c) {
                 constexpr int sub = decltype(sc)::value;
-                static_for<0, (MF > LPS ? MF : LPS)>([&](auto ic) {
+                constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+                constexpr int NM = HI - LO;
+                constexpr int NL = sub >= 0 ? LPS : 0;
+                static_for<0, (NM > NL ? NM : NL)>([&](auto ic) {
                     constexpr int i = decltype(ic)::value;
-                    if constexpr (i < MF) mfma_one(f, ic);
-                    // one load after every (MF / LPS)-th MFMA
-                    constexpr int step = MF >= LPS ? MF / LPS : 1;
-                    if constexpr (i % step == step - 1 && i / step < LPS) {
+                    if constexpr (i < NM) mfma_one(f, std::integral_constant<int, LO + i>{});
+                    // one load after every (NM / NL)-th MFMA
+                    constexpr int step = NM >= NL ? (NL > 0 ? NM / NL : 1) : 1;
+                    if constexpr (NL > 0 && i % step == step - 1 && i / step < NL) {
                         constexpr int j = sub * LPS + i / step;
                         if constexpr (j < DMA_A)
                             dma_a(j, anext, ka);
@@ -620,19 +618,28 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
                     __builtin_amdgcn_sched_barrier(0);
                 });
             };
-            substep(f0, std::integral_constant<int, 0>{});
+            using C0 = std::integral_constant<int, 0>;
+            using CM = std::integral_constant<int, MF>;
+            using CH = std::integral_constant<int, MF * 7 / 8>;
+            substep(f0, std::integral_constant<int, 0>{}, C0{}, CM{});
             load_frags(f0, abuf, bbuf, 2);
             __builtin_amdgcn_sched_barrier(0);
-            substep(f1, std::integral_constant<int, 1>{});
+            substep(f1, std::integral_constant<int, 1>{}, C0{}, CM{});
             load_frags(f1, abuf, bbuf, 3);
             __builtin_amdgcn_sched_barrier(0);
-            substep(f0, std::integral_constant<int, 2>{});
-            substep(f1, std::integral_constant<int, 3>{});
-            // A(kt+1) and B(kt+1) have landed once only B(kt+2) is outstanding
+            substep(f0, std::integral_constant<int, 2>{}, C0{}, CM{});
+            substep(f1, std::integral_constant<int, 3>{}, C0{}, CH{});
+            // A(kt+1) and B(kt+1) have landed once only B(kt+2) is outstanding;
+            // past the barrier every wave is done reading stage kt's buffers
+            // (its last fragments are in registers), which the next stage's
+            // loads overwrite
             wait_vmcnt<DMA_B>();
             __syncthreads();
             abuf = anext;
             bbuf = bbuf == 2 ? 0 : bbuf + 1;
+            load_frags(f0, abuf, bbuf, 0);  // after the last stage: read, never used
+            __builtin_amdgcn_sched_barrier(0);
+            substep(f1, std::integral_constant<int, -1>{}, CH{}, CM{});
         }
         wait_vmcnt<0>();
         __syncthreads();
@@ -647,11 +654,15 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
 
     // ---- epilogue ----
     {
-        // Straight from the accumulators: a quad transpose turns each lane's
-        // column of four rows into one row of four columns, so a lane stores 4
-        // contiguous outputs and one store instruction covers 8 rows x 32
-        // columns.
-        const int t = lane & 3, q4 = (lane & 31) >> 2;
+        // Straight from the accumulators, one value per lane and store: lane l
+        // holds column l % 32, so one store covers two rows of 32 contiguous
+        // columns (two full 128-byte lines of y, two half lines of h).  The
+        // stores go through a buffer resource over rows [row0, row0 + rows) of
+        // the output, whose range check drops the rows past the tile.
+        constexpr int OB = GATEUP ? 2 : 4;  // output bytes per element
+        const __amdgpu_buffer_rsrc_t rsrc_o = make_rsrc(
+            static_cast<unsigned char*>(a.out) + static_cast<int64_t>(row0) * a.N * OB,
+            static_cast<uint32_t>(rows * a.N * OB));
         if constexpr (FP8) {
             // per-channel scales: this lane's column of each accumulator block
 #pragma unroll
@@ -668,35 +679,32 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
                     }
             }
         }
+        const uint32_t lane_off = static_cast<uint32_t>(((4 * half) * a.N + n0 + wn * WN_OUT + r32) * OB);
+        const uint32_t row_bytes = static_cast<uint32_t>(a.N * OB);
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
             if (m >= mb_valid) continue;
             const int blk = wm + WAVES_M * m;
 #pragma unroll
             for (int n = 0; n < NB; ++n) {
-                const int col = n0 + wn * WN_OUT + n * 32 + 4 * q4;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    float v[4];
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        if constexpr (GATEUP)
-                            v[r] = silu_f32(acc[0][m][n][4 * j + r]) * acc[1][m][n][4 * j + r];
-                        else
-                            v[r] = acc[0][m][n][4 * j + r];
-                    }
-                    quad_transpose(v[0], v[1], v[2], v[3]);
-                    const int r = blk * 32 + 8 * j + 4 * half + t;
-                    if (r < rows) {
-                        const int64_t o = static_cast<int64_t>(row0 + r) * a.N + col;
-                        if constexpr (GATEUP) {
-                            const uint32_t lo = f32_to_bf16_rne(v[0]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[1])) << 16);
-                            const uint32_t hi = f32_to_bf16_rne(v[2]) | (static_cast<uint32_t>(f32_to_bf16_rne(v[3])) << 16);
-                            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = u32x2{lo, hi};
-                        } else {
-                            *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = f32x4{v[0], v[1], v[2], v[3]};
-                        }
+                for (int i = 0; i < 16; ++i) {
+                    // row blk * 32 + 8 (i / 4) + 4 half + i % 4, column n0 + wn WN_OUT + 32 n + l % 32
+                    const uint32_t off = lane_off + (blk * 32 + 8 * (i >> 2) + (i & 3)) * row_bytes + n * 32 * OB;
+                    if constexpr (GATEUP) {
+                        if (i & 1) continue;  // rows i and i + 1 are converted together
+                        typedef float f32x2 __attribute__((ext_vector_type(2)));
+                        typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+                        const float v0 = silu_f32(acc[0][m][n][i]) * acc[1][m][n][i];
+                        const float v1 = silu_f32(acc[0][m][n][i + 1]) * acc[1][m][n][i + 1];
+                        const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v0, v1}, bf16x2));
+                        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk), rsrc_o, off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk >> 16), rsrc_o, off + row_bytes, 0, 0);
+                    } else {
+                        // (copied out first: a bit cast of a vector element in place
+                        // would read element 0)
+                        const float v = acc[0][m][n][i];
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc_o, off, 0, 0);
                     }
                 }
             }
