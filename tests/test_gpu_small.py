@@ -99,6 +99,8 @@ SHAPES = [
     (5000, 128, 64, 16, 4, 2, 4),
     (2000, 512, 256, 8, 2, 1, 2),       # ~500 rows per expert: two large row tiles
     (1500, 256, 384, 16, 4, 2, 4),      # ~375 rows per expert, I not a power of two
+    (2600, 256, 128, 8, 2, 1, 2),       # ~650 rows per expert: 256 + 256 + ragged last row tile
+    (2400, 256, 128, 12, 4, 2, 2),      # ~400 rows per expert, 8 does not divide E
 ]
 
 
