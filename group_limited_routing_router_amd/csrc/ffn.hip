@@ -527,31 +527,32 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
             bf16x8 a[NA];
             bf16x8 b[NFB];
         };
-        auto load_frags = [&](Frags& f, int abuf, int bbuf, int ks) {
+        // piece q of substep ks's fragments: A blocks first, then B blocks
+        auto load_piece = [&](Frags& f, int ab, int bb, int ks, auto qc) {
+            constexpr int q = decltype(qc)::value;
             const int c = ks * 2 + half;
-            const unsigned char* sa = s_arena + (a_buf(abuf) - arena);
-            const unsigned char* sb = s_arena + (b_buf(bbuf) - arena);
-#pragma unroll
-            for (int m = 0; m < NV; ++m)
-                f.a[m] = *reinterpret_cast<const bf16x8*>(
-                    sa + frag_off((wm + WAVES_M * m) * 32 + r32, c));
-            if constexpr (NV > 0) {
-#pragma unroll
-                for (int g = 0; g < NACC; ++g)
-#pragma unroll
-                    for (int n = 0; n < NB; ++n) {
-                        const int br = g * BN_OUT + wn * WN_OUT + n * 32 + r32;
-                        if constexpr (FP8) {
-                            // 8 codes: 8-byte half (c & 1) of chunk (c >> 1)
-                            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                            const u32x2 w8 = *reinterpret_cast<const u32x2*>(
-                                sb + br * B_ROW + ((((c >> 1) ^ ((br >> 2) & 3))) << 4) + ((c & 1) << 3));
-                            f.b[g * NB + n] = e4m3x8_to_bf16x8(w8[0], w8[1]);
-                        } else {
-                            f.b[g * NB + n] = *reinterpret_cast<const bf16x8*>(sb + frag_off(br, c));
-                        }
-                    }
+            if constexpr (q < NV) {
+                const unsigned char* sa = s_arena + (a_buf(ab) - arena);
+                f.a[q] = *reinterpret_cast<const bf16x8*>(sa + frag_off((wm + WAVES_M * q) * 32 + r32, c));
+            } else if constexpr (NV > 0) {
+                constexpr int gn = q - NV;
+                constexpr int g = gn / NB, n = gn % NB;
+                const unsigned char* sb = s_arena + (b_buf(bb) - arena);
+                const int br = g * BN_OUT + wn * WN_OUT + n * 32 + r32;
+                if constexpr (FP8) {
+                    // 8 codes: 8-byte half (c & 1) of chunk (c >> 1)
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    const u32x2 w8 = *reinterpret_cast<const u32x2*>(
+                        sb + br * B_ROW + ((((c >> 1) ^ ((br >> 2) & 3))) << 4) + ((c & 1) << 3));
+                    f.b[gn] = e4m3x8_to_bf16x8(w8[0], w8[1]);
+                } else {
+                    f.b[gn] = *reinterpret_cast<const bf16x8*>(sb + frag_off(br, c));
+                }
             }
+        };
+        constexpr int NP = NV > 0 ? NV + NFB : 0;  // fragment pieces per substep
+        auto load_frags = [&](Frags& f, int ab, int bb, int ks) {
+            static_for<0, NP>([&](auto qc) { load_piece(f, ab, bb, ks, qc); });
         };
         auto mfma_one = [&](const Frags& f, auto ic) {
             constexpr int i = decltype(ic)::value;      // i = (g * NB + n) * NV + m
@@ -559,9 +560,6 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
             constexpr int gn = i / (NV > 0 ? NV : 1);
             constexpr int g = gn / NB, n = gn % NB;
             if constexpr (NV > 0) acc[g][m][n] = mfma32(f.a[m], f.b[gn], acc[g][m][n]);
-        };
-        auto mfmas = [&](const Frags& f) {
-            static_for<0, MF>([&](auto ic) { mfma_one(f, ic); });
         };
         const int nk = K / BK;
         // prologue: A(0), B(0), B(1) in flight; wait for the first two
@@ -582,31 +580,38 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
             const int anext = abuf ^ 1;
             const int bnext = bbuf == 0 ? 2 : bbuf - 1;     // (bbuf + 2) % 3
             // Phases are pinned with scheduling fences (the compiler would
-            // otherwise sink fragment reads next to their MFMAs): fragment
-            // reads of a substep are issued one substep ahead, and the
-            // stage's loads are spread evenly over its MFMAs up to the stage
-            // barrier (activations first, they are needed one stage ahead;
-            // weights after), so the texture unit never backs up into the
-            // MFMA issue stream.  The stage barrier sits before the last
-            // eighth of the last substep's MFMAs: the first fragments of the
-            // next stage are read while those run, so the matrix pipe does
-            // not wait out a whole LDS round trip at every stage (a later
-            // barrier leaves the loads of the next stage more time to land).
-            load_frags(f1, abuf, bbuf, 1);
-            __builtin_amdgcn_sched_barrier(0);
+            // otherwise sink fragment reads next to their MFMAs or bunch them):
+            // the fragments of the next substep are read one at a time between
+            // the MFMAs of this one (A first, then B, in order of first use),
+            // and the stage's loads are spread evenly over its MFMAs up to the
+            // stage barrier (activations first, they are needed one stage
+            // ahead; weights after), so neither the LDS nor the texture unit
+            // backs up into the MFMA issue stream.  The stage barrier sits
+            // before the last eighth of the last substep's MFMAs: the first
+            // fragments of the next stage are read while those run, so the
+            // matrix pipe does not wait out a whole LDS round trip at every
+            // stage (a later barrier leaves the loads of the next stage more
+            // time to land).
             constexpr int LPS = (DMA_A + DMA_B) / 4;  // loads per substep (4, FP8: 3)
             static_assert(LPS * 4 == DMA_A + DMA_B, "loads split evenly over the substeps");
-            // MFMAs [LO, HI) of substep SUB; a negative SUB issues no loads,
-            // else that substep's loads are spread over these MFMAs
-            auto substep = [&](const Frags& f, auto sc, auto lo_c, auto hi_c) {
+            // MFMAs [LO, HI) of substep SUB with its stage loads spread over them
+            // (none for a negative SUB) and, for KN >= 0, the fragments of
+            // substep KN read into FN piece by piece between them
+            auto substep = [&](const Frags& f, auto sc, auto lo_c, auto hi_c, Frags& fn, auto kn_c) {
                 constexpr int sub = decltype(sc)::value;
                 constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
+                constexpr int KN = decltype(kn_c)::value;
                 constexpr int NM = HI - LO;
                 constexpr int NL = sub >= 0 ? LPS : 0;
-                static_for<0, (NM > NL ? NM : NL)>([&](auto ic) {
+                constexpr int NPC = KN >= 0 ? NP : 0;
+                constexpr int IT = NM > NL ? (NM > 0 ? NM : 1) : (NL > 0 ? NL : 1);
+                static_for<0, IT>([&](auto ic) {
                     constexpr int i = decltype(ic)::value;
+                    static_for<0, NPC>([&](auto qc) {
+                        constexpr int q = decltype(qc)::value;
+                        if constexpr (q * IT / (NPC > 0 ? NPC : 1) == i) load_piece(fn, abuf, bbuf, KN, qc);
+                    });
                     if constexpr (i < NM) mfma_one(f, std::integral_constant<int, LO + i>{});
-                    // one load after every (NM / NL)-th MFMA
                     constexpr int step = NM >= NL ? (NL > 0 ? NM / NL : 1) : 1;
                     if constexpr (NL > 0 && i % step == step - 1 && i / step < NL) {
                         constexpr int j = sub * LPS + i / step;
@@ -621,25 +626,18 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
             using C0 = std::integral_constant<int, 0>;
             using CM = std::integral_constant<int, MF>;
             using CH = std::integral_constant<int, MF * 7 / 8>;
-            substep(f0, std::integral_constant<int, 0>{}, C0{}, CM{});
-            load_frags(f0, abuf, bbuf, 2);
-            __builtin_amdgcn_sched_barrier(0);
-            substep(f1, std::integral_constant<int, 1>{}, C0{}, CM{});
-            load_frags(f1, abuf, bbuf, 3);
-            __builtin_amdgcn_sched_barrier(0);
-            substep(f0, std::integral_constant<int, 2>{}, C0{}, CM{});
-            substep(f1, std::integral_constant<int, 3>{}, C0{}, CH{});
-            // A(kt+1) and B(kt+1) have landed once only B(kt+2) is outstanding;
-            // past the barrier every wave is done reading stage kt's buffers
-            // (its last fragments are in registers), which the next stage's
-            // loads overwrite
+            using KNone = std::integral_constant<int, -1>;
+            substep(f0, std::integral_constant<int, 0>{}, C0{}, CM{}, f1, std::integral_constant<int, 1>{});
+            substep(f1, std::integral_constant<int, 1>{}, C0{}, CM{}, f0, std::integral_constant<int, 2>{});
+            substep(f0, std::integral_constant<int, 2>{}, C0{}, CM{}, f1, std::integral_constant<int, 3>{});
+            substep(f1, std::integral_constant<int, 3>{}, C0{}, CH{}, f0, KNone{});
             wait_vmcnt<DMA_B>();
             __syncthreads();
             abuf = anext;
             bbuf = bbuf == 2 ? 0 : bbuf + 1;
             load_frags(f0, abuf, bbuf, 0);  // after the last stage: read, never used
             __builtin_amdgcn_sched_barrier(0);
-            substep(f1, std::integral_constant<int, -1>{}, CH{}, CM{});
+            substep(f1, std::integral_constant<int, -1>{}, CH{}, CM{}, f0, KNone{});
         }
         wait_vmcnt<0>();
         __syncthreads();
