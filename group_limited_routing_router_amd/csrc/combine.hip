@@ -17,12 +17,25 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// y larger than this streams past the caches (nontemporal loads and output
+// stores): at prefill it is far larger than L2 plus the Infinity Cache and is
+// read once; at decode it is still cache-resident from the down projection.
+constexpr int64_t kStreamBytes = static_cast<int64_t>(256) << 20;
+
+__device__ __forceinline__ float4 load4(const float* p, bool nt) {
+    if (nt) {
+        const f32x4 v = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+        return make_float4(v[0], v[1], v[2], v[3]);
+    }
+    return *reinterpret_cast<const float4*>(p);
+}
+
 template <int K, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int H, float scale,
                                                            const float* __restrict__ y,
                                                            const int32_t* __restrict__ pair_rows,
                                                            const float* __restrict__ weights,
-                                                           void* __restrict__ out) {
+                                                           void* __restrict__ out, bool nt) {
     const int64_t t = blockIdx.x;
     int32_t row[K];
     float w[K];
@@ -37,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int H, flo
 #pragma unroll
         for (int j = 0; j < K; ++j) {
             if (row[j] >= 0)
-                v[j] = reinterpret_cast<const float4*>(y + static_cast<int64_t>(row[j]) * H)[c];
+                v[j] = load4(y + static_cast<int64_t>(row[j]) * H + 4 * c, nt);
             else
                 v[j] = make_float4(0.f, 0.f, 0.f, 0.f);
         }
@@ -61,7 +74,11 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int H, flo
                        (static_cast<uint32_t>(f32_to_bf16_rne(acc.w)) << 16);
             reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + t * H)[c] = packed;
         } else {
-            reinterpret_cast<float4*>(static_cast<float*>(out) + t * H)[c] = acc;
+            float* o = static_cast<float*>(out) + t * H + 4 * c;
+            if (nt)
+                __builtin_nontemporal_store(f32x4{acc.x, acc.y, acc.z, acc.w}, reinterpret_cast<f32x4*>(o));
+            else
+                *reinterpret_cast<float4*>(o) = acc;
         }
     }
 }
@@ -70,10 +87,11 @@ template <int K>
 hipError_t launch_k(const Problem& p, const float* y, const int32_t* pair_rows,
                     const float* weights, void* out, bool out_bf16, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(p.T)), block(kThreads);
+    const bool nt = p.T * p.k * static_cast<int64_t>(p.H) * 4 > kStreamBytes;
     if (out_bf16)
-        combine_kernel<K, true><<<grid, block, 0, s>>>(p.T, p.H, p.scale, y, pair_rows, weights, out);
+        combine_kernel<K, true><<<grid, block, 0, s>>>(p.T, p.H, p.scale, y, pair_rows, weights, out, nt);
     else
-        combine_kernel<K, false><<<grid, block, 0, s>>>(p.T, p.H, p.scale, y, pair_rows, weights, out);
+        combine_kernel<K, false><<<grid, block, 0, s>>>(p.T, p.H, p.scale, y, pair_rows, weights, out, nt);
     return hipGetLastError();
 }
 
@@ -90,7 +108,8 @@ template <int K, int NC>
 __global__ __launch_bounds__(kThreads) void combine_residual_kernel(
     int64_t T, int H, float scale, const float* __restrict__ y,
     const int32_t* __restrict__ pair_rows, const float* __restrict__ weights,
-    const float* __restrict__ gain, float eps, float wa, float wb, float* __restrict__ res) {
+    const float* __restrict__ gain, float eps, float wa, float wb, float* __restrict__ res,
+    bool nt) {
     __shared__ float s_part[kThreads / 64];
     const int64_t t = blockIdx.x;
     int32_t row[K];
@@ -112,7 +131,7 @@ __global__ __launch_bounds__(kThreads) void combine_residual_kernel(
 #pragma unroll
             for (int j = 0; j < K; ++j) {
                 if (row[j] < 0) continue;
-                const float4 v = reinterpret_cast<const float4*>(y + static_cast<int64_t>(row[j]) * H)[c];
+                const float4 v = load4(y + static_cast<int64_t>(row[j]) * H + 4 * c, nt);
                 acc.x = acc.x + w[j] * v.x;
                 acc.y = acc.y + w[j] * v.y;
                 acc.z = acc.z + w[j] * v.z;
@@ -160,9 +179,10 @@ hipError_t launch_residual_k(const Problem& p, const float* y, const int32_t* pa
                              float wb, float* res, hipStream_t s) {
     const dim3 grid(static_cast<unsigned>(p.T)), block(kThreads);
     const int chunks = (p.H / 4 + kThreads - 1) / kThreads;
+    const bool nt = p.T * p.k * static_cast<int64_t>(p.H) * 4 > kStreamBytes;
 #define MOE_RES(NC)                                                                       \
     combine_residual_kernel<K, NC><<<grid, block, 0, s>>>(p.T, p.H, p.scale, y, pair_rows, \
-                                                          weights, gain, eps, wa, wb, res)
+                                                          weights, gain, eps, wa, wb, res, nt)
     if (chunks <= 1) MOE_RES(1);
     else if (chunks <= 2) MOE_RES(2);
     else if (chunks <= 4) MOE_RES(4);
