@@ -17,10 +17,10 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// y larger than this streams past the caches (nontemporal loads and output
-// stores): at prefill it is far larger than L2 plus the Infinity Cache and is
-// read once; at decode it is still cache-resident from the down projection.
-constexpr int64_t kStreamBytes = static_cast<int64_t>(256) << 20;
+// y larger than kStreamBytes streams past the caches (nontemporal loads and
+// output stores): at prefill it is far larger than L2 plus the Infinity Cache
+// and is read once; at decode it is still cache-resident from the down
+// projection.
 
 __device__ __forceinline__ float4 load4(const float* p, bool nt) {
     if (nt) {

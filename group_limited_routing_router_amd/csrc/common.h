@@ -13,6 +13,9 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kNumXcd = 8;  // MI355X: workgroups go round-robin over 8 XCDs
+// Intermediate buffers larger than the Infinity Cache (256 MB on MI355X) that
+// are written once and read once stream past the caches.
+constexpr int64_t kStreamBytes = static_cast<int64_t>(256) << 20;
 
 // bf16 bit pattern -> fp32 (exact).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {

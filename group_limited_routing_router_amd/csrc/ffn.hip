@@ -72,6 +72,7 @@ struct FfnArgs {
     void* out;               // h [P,I] bf16 (gate/up) or y [P,H] fp32 (down)
     const float* s0;         // FP8 weights only: per-channel scales of b0 [E,N]
     const float* s1;         // and of b1
+    bool stream_out = false; // large-tile down: y stores stream past the caches
 };
 
 // Map this workgroup to a tile (expert e, column tile nt, row range
@@ -661,51 +662,74 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
         const __amdgpu_buffer_rsrc_t rsrc_o = make_rsrc(
             static_cast<unsigned char*>(a.out) + static_cast<int64_t>(row0) * a.N * OB,
             static_cast<uint32_t>(rows * a.N * OB));
-        if constexpr (FP8) {
-            // per-channel scales: this lane's column of each accumulator block
+        // FP8: per-channel scales of this lane's column of each accumulator
+        // block, applied as each accumulator is read
+        float sc0[NB], sc1[NB];
 #pragma unroll
-            for (int n = 0; n < NB; ++n) {
-                const int64_t ch = static_cast<int64_t>(e) * a.N + n0 + wn * WN_OUT + n * 32 + r32;
-                const float s0 = a.s0[ch];
-                const float s1 = GATEUP ? a.s1[ch] : 1.0f;
-#pragma unroll
-                for (int m = 0; m < MB; ++m)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        acc[0][m][n][i] = s0 * acc[0][m][n][i];
-                        if constexpr (GATEUP) acc[1][m][n][i] = s1 * acc[1][m][n][i];
-                    }
-            }
+        for (int n = 0; n < NB; ++n) {
+            const int64_t ch = static_cast<int64_t>(e) * a.N + n0 + wn * WN_OUT + n * 32 + r32;
+            sc0[n] = FP8 ? a.s0[ch] : 1.0f;
+            sc1[n] = (FP8 && GATEUP) ? a.s1[ch] : 1.0f;
         }
         const uint32_t lane_off = static_cast<uint32_t>(((4 * half) * a.N + n0 + wn * WN_OUT + r32) * OB);
         const uint32_t row_bytes = static_cast<uint32_t>(a.N * OB);
+        if constexpr (GATEUP) {
 #pragma unroll
-        for (int m = 0; m < MB; ++m) {
-            if (m >= mb_valid) continue;
-            const int blk = wm + WAVES_M * m;
+            for (int m = 0; m < MB; ++m) {
+                if (m >= mb_valid) continue;
+                const int blk = wm + WAVES_M * m;
 #pragma unroll
-            for (int n = 0; n < NB; ++n) {
+                for (int n = 0; n < NB; ++n) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    // row blk * 32 + 8 (i / 4) + 4 half + i % 4, column n0 + wn WN_OUT + 32 n + l % 32
-                    const uint32_t off = lane_off + (blk * 32 + 8 * (i >> 2) + (i & 3)) * row_bytes + n * 32 * OB;
-                    if constexpr (GATEUP) {
-                        if (i & 1) continue;  // rows i and i + 1 are converted together
+                    for (int i = 0; i < 16; i += 2) {
+                        // rows blk * 32 + 8 (i / 4) + 4 half + i % 4 and the next,
+                        // column n0 + wn WN_OUT + 32 n + l % 32, converted together
+                        const uint32_t off = lane_off + (blk * 32 + 8 * (i >> 2) + (i & 3)) * row_bytes + n * 32 * OB;
                         typedef float f32x2 __attribute__((ext_vector_type(2)));
                         typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-                        const float v0 = silu_f32(acc[0][m][n][i]) * acc[1][m][n][i];
-                        const float v1 = silu_f32(acc[0][m][n][i + 1]) * acc[1][m][n][i + 1];
+                        float g0 = acc[0][m][n][i], g1 = acc[0][m][n][i + 1];
+                        float u0 = acc[1][m][n][i], u1 = acc[1][m][n][i + 1];
+                        if constexpr (FP8) {
+                            g0 *= sc0[n];
+                            g1 *= sc0[n];
+                            u0 *= sc1[n];
+                            u1 *= sc1[n];
+                        }
+                        const float v0 = silu_f32(g0) * u0;
+                        const float v1 = silu_f32(g1) * u1;
                         const uint32_t pk = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{v0, v1}, bf16x2));
                         __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk), rsrc_o, off, 0, 0);
                         __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pk >> 16), rsrc_o, off + row_bytes, 0, 0);
-                    } else {
-                        // (copied out first: a bit cast of a vector element in place
-                        // would read element 0)
-                        const float v = acc[0][m][n][i];
-                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc_o, off, 0, 0);
                     }
                 }
             }
+        } else {
+            // y larger than the caches is written nontemporally (cache policy
+            // nt): the combine reads it once, long after
+            auto store_y = [&](auto nt_c) {
+                constexpr int kPolicy = decltype(nt_c)::value ? 2 : 0;
+#pragma unroll
+                for (int m = 0; m < MB; ++m) {
+                    if (m >= mb_valid) continue;
+                    const int blk = wm + WAVES_M * m;
+#pragma unroll
+                    for (int n = 0; n < NB; ++n)
+#pragma unroll
+                        for (int i = 0; i < 16; ++i) {
+                            // row blk * 32 + 8 (i / 4) + 4 half + i % 4, column n0 + wn WN_OUT + 32 n + l % 32
+                            const uint32_t off = lane_off + (blk * 32 + 8 * (i >> 2) + (i & 3)) * row_bytes + n * 32 * OB;
+                            // (copied out first: a bit cast of a vector element in
+                            // place would read element 0)
+                            float v = acc[0][m][n][i];
+                            if constexpr (FP8) v *= sc0[n];
+                            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rsrc_o, off, 0, kPolicy);
+                        }
+                }
+            };
+            if (a.stream_out)
+                store_y(std::true_type{});
+            else
+                store_y(std::false_type{});
         }
     }
 }
@@ -742,8 +766,9 @@ hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* so
 hipError_t launch_down(const Problem& p, const uint16_t* h, const int32_t* offsets,
                        const uint16_t* w_down, float* y, hipStream_t s) {
     const int64_t P = p.T * p.k;
-    const FfnArgs a{P, p.T, p.k, p.E, p.I, p.H, h, nullptr, offsets, w_down, nullptr, y, nullptr,
-                    nullptr};
+    FfnArgs a{P, p.T, p.k, p.E, p.I, p.H, h, nullptr, offsets, w_down, nullptr, y, nullptr,
+              nullptr};
+    a.stream_out = P * static_cast<int64_t>(p.H) * 4 > kStreamBytes;
     const int64_t rows_per_expert = P / p.E;
     if (rows_per_expert <= 24) return launch_gemm<16, 64, 1, 4, false>(a, s);
     if (rows_per_expert <= 96 || p.H % 256 != 0 || p.I % 128 != 0)
@@ -780,8 +805,9 @@ hipError_t launch_expert_ffn_fp8(const Problem& p, const uint16_t* x, const int3
     else
         err = launch_gemm_dma<true, true>(gu, s);
     if (err != hipSuccess) return err;
-    const FfnArgs dn{P, p.T, p.k, p.E, p.I, p.H, h, nullptr, offsets, w_down, nullptr, y, s_down,
-                     nullptr};
+    FfnArgs dn{P, p.T, p.k, p.E, p.I, p.H, h, nullptr, offsets, w_down, nullptr, y, s_down,
+               nullptr};
+    dn.stream_out = P * static_cast<int64_t>(p.H) * 4 > kStreamBytes;
     if (rows_per_expert <= 24 && p.H % 128 == 0) return launch_gemm<16, 128, 1, 4, false, true>(dn, s);
     if (rows_per_expert <= 96 || p.H % 256 != 0 || p.I % 128 != 0)
         return launch_gemm<64, 128, 1, 4, false, true>(dn, s);
