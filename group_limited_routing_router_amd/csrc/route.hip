@@ -265,7 +265,7 @@ hipError_t launch_route(const Problem& p, const uint16_t* x, const uint16_t* w_r
     if (p.T >= 4096) {
         // many tokens: 32-token tiles (the router weight is read once per tile)
         const int64_t grid = (p.T + 31) / 32;
-        route_kernel<2, 8, 3><<<dim3(static_cast<unsigned>(grid)), dim3(512), 0, s>>>(
+        route_kernel<2, 8, 6><<<dim3(static_cast<unsigned>(grid)), dim3(512), 0, s>>>(
             p.T, p.H, p.E, p.G, p.TG, p.k, 32, x, w_router, bias, ids, weights);
     } else {
         // few tokens: a workgroup takes only as many tokens (a power of two up
