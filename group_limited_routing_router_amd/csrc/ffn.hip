@@ -524,9 +524,14 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
         constexpr int NV = decltype(nv_tag)::value;
         constexpr int NA = NV > 0 ? NV : 1;
         constexpr int MF = NV * NFB;  // MFMAs per substep
+        // B fragments are held as read: bf16, or 8 E4M3 codes widened to bf16
+        // right before the MFMAs that use them (converting at the read would
+        // wait out the LDS latency there)
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        typedef typename std::conditional<FP8, u32x2, bf16x8>::type BFrag;
         struct Frags {
             bf16x8 a[NA];
-            bf16x8 b[NFB];
+            BFrag b[NFB];
         };
         // piece q of substep ks's fragments: A blocks first, then B blocks
         auto load_piece = [&](Frags& f, int ab, int bb, int ks, auto qc) {
@@ -542,10 +547,8 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
                 const int br = g * BN_OUT + wn * WN_OUT + n * 32 + r32;
                 if constexpr (FP8) {
                     // 8 codes: 8-byte half (c & 1) of chunk (c >> 1)
-                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                    const u32x2 w8 = *reinterpret_cast<const u32x2*>(
+                    f.b[gn] = *reinterpret_cast<const u32x2*>(
                         sb + br * B_ROW + ((((c >> 1) ^ ((br >> 2) & 3))) << 4) + ((c & 1) << 3));
-                    f.b[gn] = e4m3x8_to_bf16x8(w8[0], w8[1]);
                 } else {
                     f.b[gn] = *reinterpret_cast<const bf16x8*>(sb + frag_off(br, c));
                 }
@@ -555,12 +558,23 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
         auto load_frags = [&](Frags& f, int ab, int bb, int ks) {
             static_for<0, NP>([&](auto qc) { load_piece(f, ab, bb, ks, qc); });
         };
-        auto mfma_one = [&](const Frags& f, auto ic) {
-            constexpr int i = decltype(ic)::value;      // i = (g * NB + n) * NV + m
+        // MFMA i = (g * NB + n) * NV + m of a substep; bop holds B fragment gn
+        // in bf16 (FIRST: MFMA i is the first of a run on it, so it is
+        // widened here)
+        auto mfma_one = [&](const Frags& f, auto ic, bf16x8& bop, bool first) {
+            constexpr int i = decltype(ic)::value;
             constexpr int m = i % (NV > 0 ? NV : 1);
             constexpr int gn = i / (NV > 0 ? NV : 1);
             constexpr int g = gn / NB, n = gn % NB;
-            if constexpr (NV > 0) acc[g][m][n] = mfma32(f.a[m], f.b[gn], acc[g][m][n]);
+            if constexpr (NV > 0) {
+                if (m == 0 || first) {  // compile-time at every call site
+                    if constexpr (FP8)
+                        bop = e4m3x8_to_bf16x8(f.b[gn][0], f.b[gn][1]);
+                    else
+                        bop = f.b[gn];
+                }
+                acc[g][m][n] = mfma32(f.a[m], bop, acc[g][m][n]);
+            }
         };
         const int nk = K / BK;
         // prologue: A(0), B(0), B(1) in flight; wait for the first two
@@ -606,13 +620,14 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
                 constexpr int NL = sub >= 0 ? LPS : 0;
                 constexpr int NPC = KN >= 0 ? NP : 0;
                 constexpr int IT = NM > NL ? (NM > 0 ? NM : 1) : (NL > 0 ? NL : 1);
+                bf16x8 bop;
                 static_for<0, IT>([&](auto ic) {
                     constexpr int i = decltype(ic)::value;
                     static_for<0, NPC>([&](auto qc) {
                         constexpr int q = decltype(qc)::value;
                         if constexpr (q * IT / (NPC > 0 ? NPC : 1) == i) load_piece(fn, abuf, bbuf, KN, qc);
                     });
-                    if constexpr (i < NM) mfma_one(f, std::integral_constant<int, LO + i>{});
+                    if constexpr (i < NM) mfma_one(f, std::integral_constant<int, LO + i>{}, bop, i == 0);
                     constexpr int step = NM >= NL ? (NL > 0 ? NM / NL : 1) : 1;
                     if constexpr (NL > 0 && i % step == step - 1 && i / step < NL) {
                         constexpr int j = sub * LPS + i / step;
