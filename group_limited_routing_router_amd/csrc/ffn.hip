@@ -10,23 +10,21 @@
 //             X_q = x[sorted_pairs[q] / k]  (rows gathered on the fly)
 //   down:     y[q, m] = h[q] . Wd[e,m]      (fp32 out)
 //
-// One kernel template serves both.  A workgroup (4 waves) computes a BM x BN
-// tile of one expert: BM sorted rows by BN weight rows.  For gate/up the BN
-// weight rows are BN/2 gate rows and the BN/2 up rows of the same output
-// columns, so a lane holds gate and up accumulators of the same (row, col)
-// and the SwiGLU epilogue needs no data exchange.  Tiles of 64 along K are
-// staged through LDS with two buffers; global loads of tile k+1 are in flight
-// while the MFMAs of tile k run.  LDS rows are padded by 16 B so the 16-row
-// MFMA operand reads hit distinct banks.
+// Two kernels serve both projections.  A workgroup (4 waves) computes a tile
+// of one expert: BM sorted rows by BN weight rows.  For gate/up the BN weight
+// rows are BN/2 gate rows and the BN/2 up rows of the same output columns, so
+// a lane holds gate and up accumulators of the same (row, col) and the SwiGLU
+// epilogue needs no data exchange.
+//   ffn_gemm_kernel      16- or 64-row tiles (few rows per expert: decode),
+//                        16x16x32 MFMA, K staged 64 at a time through two
+//                        padded LDS buffers via registers.
+//   ffn_gemm_dma_kernel  256 x 256 tiles (many rows per expert: prefill),
+//                        32x32x16 MFMA, operands loaded straight into LDS.
 //
 // The tile list is data-dependent and never read back by the host: the grid
 // is an upper bound, every workgroup rebuilds the per-expert tile prefix sum
 // from expert_offsets in LDS and maps itself to a tile, and surplus
-// workgroups exit.  The mapping is XCD-aware: workgroup b runs on XCD b % 8,
-// and each XCD receives one contiguous run of the tile list (expert-major,
-// then column tile, then row tile), so the tiles of one expert share its
-// gathered activations and, across row tiles, its weight tiles in that XCD's
-// L2.
+// workgroups exit.  The mapping is XCD-aware (see find_tile).
 #include <type_traits>
 
 #include "common.h"
