@@ -36,8 +36,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kMaxE = 256;
-constexpr int BK = 64;           // K elements per LDS stage
-constexpr int LDS_STRIDE = BK + 8;  // bf16 per LDS row (16 B pad)
+constexpr int BK = 64;           // K elements per LDS stage (large-tile kernel)
 
 // Raw buffer resource over [base, base + bytes): 32-bit offsets from one
 // scalar base; loads past `bytes` return zero.  Third dword: gfx9 default.
@@ -169,12 +168,16 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 }
 
 // FP8 = true: the weights are E4M3 codes with one fp32 scale per output
-// channel (FfnArgs::s0/s1).  They are staged in LDS as codes (64 bytes a row
-// and stage), widened to bf16 as each MFMA operand is read, and the channel
-// scale multiplies the fp32 accumulator in the epilogue.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP, bool FP8 = false>
+// channel (FfnArgs::s0/s1).  They are staged in LDS as codes, widened to bf16
+// as each MFMA operand is read, and the channel scale multiplies the fp32
+// accumulator in the epilogue.  SK is the K extent of an LDS stage: 128 for
+// FP8 weights, so that every weight row of a stage is one whole 128-byte line.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP, bool FP8 = false, int SK = 64>
 __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     static_assert(WAVES_M * WAVES_N == kWaves, "4 waves");
+    static_assert(SK == 64 || SK == 128, "stage depth");
+    constexpr int A_STRIDE = SK + 8;                  // bf16 per LDS activation row (16 B pad)
+    constexpr int A_CPR = SK / 8;                     // 16-byte chunks per activation row
     constexpr int BN_OUT = GATEUP ? BN / 2 : BN;     // output columns per tile
     constexpr int WM = BM / WAVES_M;                  // rows per wave
     constexpr int MB = WM / 16;
@@ -182,16 +185,16 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     constexpr int NB = WN_OUT / 16;
     static_assert(MB >= 1 && NB >= 1, "tile too small");
     constexpr int EB = FP8 ? 1 : 2;                   // bytes per weight
-    constexpr int B_ROW = BK * EB;                    // weight bytes per row and stage
+    constexpr int B_ROW = SK * EB;                    // weight bytes per row and stage
     constexpr int B_STRIDE = B_ROW + 16;              // LDS row pitch of the weight stage
     constexpr int B_CPR = B_ROW / 16;                 // 16-byte chunks per weight row
-    constexpr int A_CHUNKS = BM * (BK / 8);           // 16-byte chunks per stage
+    constexpr int A_CHUNKS = BM * A_CPR;              // 16-byte chunks per stage
     constexpr int B_CHUNKS = BN * B_CPR;
     constexpr int A_ITERS = (A_CHUNKS + kThreads - 1) / kThreads;
     constexpr int B_ITERS = B_CHUNKS / kThreads;
     static_assert(B_CHUNKS % kThreads == 0, "B tile");
 
-    __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * LDS_STRIDE];
+    __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * A_STRIDE];
     __shared__ __attribute__((aligned(16))) unsigned char s_b[2][BN * B_STRIDE];
     __shared__ int32_t s_off[kMaxE + 1];
     __shared__ int32_t s_tstart[kMaxE + 1];
@@ -205,12 +208,12 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     const int n0 = nt * BN_OUT;
     const int K = a.K;
 
-    // ---- loader addressing: chunk c -> (row c/8, 16-byte column c%8) ----
+    // ---- loader addressing: chunk c -> (row c / A_CPR, 16-byte column c % A_CPR) ----
     const uint16_t* a_ptr[A_ITERS];
 #pragma unroll
     for (int i = 0; i < A_ITERS; ++i) {
         const int c = tid + i * kThreads;
-        const int r = min(c >> 3, rows - 1);
+        const int r = min(c / A_CPR, rows - 1);
         int64_t src_row;
         if constexpr (GATEUP) {
             int64_t tok = a.sorted_pairs[row0 + r] / a.k;
@@ -219,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
         } else {
             src_row = row0 + r;
         }
-        a_ptr[i] = a.a_src + src_row * K + (c & 7) * 8;
+        a_ptr[i] = a.a_src + src_row * K + (c % A_CPR) * 8;
     }
     const unsigned char* b_ptr[B_ITERS];
 #pragma unroll
@@ -241,7 +244,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
 
     u32x4 ra[A_ITERS], rb[B_ITERS];
     auto load_global = [&](int kt) {
-        const int koff = kt * BK;
+        const int koff = kt * SK;
 #pragma unroll
         for (int i = 0; i < A_ITERS; ++i)
             if (A_CHUNKS % kThreads == 0 || tid + i * kThreads < A_CHUNKS) ra[i] = ld16(a_ptr[i] + koff);
@@ -253,7 +256,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
         for (int i = 0; i < A_ITERS; ++i) {
             const int c = tid + i * kThreads;
             if (A_CHUNKS % kThreads == 0 || c < A_CHUNKS)
-                *reinterpret_cast<u32x4*>(&s_a[buf][(c >> 3) * LDS_STRIDE + (c & 7) * 8]) = ra[i];
+                *reinterpret_cast<u32x4*>(&s_a[buf][(c / A_CPR) * A_STRIDE + (c % A_CPR) * 8]) = ra[i];
         }
 #pragma unroll
         for (int i = 0; i < B_ITERS; ++i) {
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
 #pragma unroll
             for (int n = 0; n < NB; ++n) acc[g][m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const int nk = K / BK;
+    const int nk = K / SK;
     load_global(0);
     store_lds(0);
     __syncthreads();
@@ -283,12 +286,12 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
         const uint16_t* sa = s_a[buf];
         const unsigned char* sb = s_b[buf];
 #pragma unroll
-        for (int ks = 0; ks < BK / 32; ++ks) {
+        for (int ks = 0; ks < SK / 32; ++ks) {
             const int kof = ks * 32 + q * 8;
             bf16x8 af[MB];
 #pragma unroll
             for (int m = 0; m < MB; ++m)
-                af[m] = *reinterpret_cast<const bf16x8*>(&sa[(wm * WM + m * 16 + r16) * LDS_STRIDE + kof]);
+                af[m] = *reinterpret_cast<const bf16x8*>(&sa[(wm * WM + m * 16 + r16) * A_STRIDE + kof]);
 #pragma unroll
             for (int g = 0; g < NACC; ++g) {
 #pragma unroll
@@ -348,7 +351,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP, bool FP8 = false>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP, bool FP8 = false, int SK = 64>
 hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
     constexpr int BN_OUT = GATEUP ? BN / 2 : BN;
     const int64_t mtiles = (a.P + BM - 1) / BM + (a.E < a.P ? a.E : a.P);
@@ -356,7 +359,7 @@ hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
     const int64_t grid = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    ffn_gemm_kernel<BM, BN, WAVES_M, WAVES_N, GATEUP, FP8>
+    ffn_gemm_kernel<BM, BN, WAVES_M, WAVES_N, GATEUP, FP8, SK>
         <<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();
 }
@@ -768,7 +771,9 @@ hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* so
     const FfnArgs a{P, p.T, p.k, p.E, p.H, p.I, x, sorted_pairs, offsets, w_gate, w_up, h,
                     nullptr, nullptr};
     const int64_t rows_per_expert = P / p.E;
-    if (rows_per_expert <= 24) return launch_gemm<16, 128, 1, 4, true>(a, s);
+    // weight streaming in stages of K = 128 (H % 128 == 0 holds for every
+    // accepted problem)
+    if (rows_per_expert <= 24) return launch_gemm<16, 128, 1, 4, true, false, 128>(a, s);
     // the large-tile kernel addresses x with 32-bit buffer offsets
     const bool x_fits = p.T * static_cast<int64_t>(p.H) * 2 < (static_cast<int64_t>(1) << 31);
     if (rows_per_expert <= 96 || p.I % 128 != 0 || !x_fits)
@@ -783,7 +788,11 @@ hipError_t launch_down(const Problem& p, const uint16_t* h, const int32_t* offse
               nullptr};
     a.stream_out = P * static_cast<int64_t>(p.H) * 4 > kStreamBytes;
     const int64_t rows_per_expert = P / p.E;
-    if (rows_per_expert <= 24) return launch_gemm<16, 64, 1, 4, false>(a, s);
+    if (rows_per_expert <= 24) {
+        // stages of K = 128 where I allows
+        if (p.I % 128 == 0) return launch_gemm<16, 64, 1, 4, false, false, 128>(a, s);
+        return launch_gemm<16, 64, 1, 4, false>(a, s);
+    }
     if (rows_per_expert <= 96 || p.H % 256 != 0 || p.I % 128 != 0)
         return launch_gemm<64, 128, 1, 4, false>(a, s);
     return launch_gemm_dma<false>(a, s);
@@ -807,23 +816,26 @@ hipError_t launch_expert_ffn_fp8(const Problem& p, const uint16_t* x, const int3
     const int64_t rows_per_expert = P / p.E;
     const FfnArgs gu{P, p.T, p.k, p.E, p.H, p.I, x, sorted_pairs, offsets, w_gate, w_up, h,
                      s_gate, s_up};
-    // few rows per expert: the weight stream is the cost, so a tile takes
-    // twice the weight rows of the bf16 kernels (the same bytes per stage)
+    // few rows per expert: the weight stream is the cost; stages of K = 128
+    // make every weight row of a stage one whole 128-byte line (gate/up: K = H,
+    // and H % 128 == 0 holds for every accepted problem; down: where I allows)
     const bool x_fits = p.T * static_cast<int64_t>(p.H) * 2 < (static_cast<int64_t>(1) << 31);
     hipError_t err;
-    if (rows_per_expert <= 24 && p.I % 128 == 0)
-        err = launch_gemm<16, 256, 1, 4, true, true>(gu, s);
+    if (rows_per_expert <= 24)
+        err = launch_gemm<16, 128, 1, 4, true, true, 128>(gu, s);
     else if (rows_per_expert <= 96 || p.I % 128 != 0 || !x_fits)
-        err = launch_gemm<64, 128, 1, 4, true, true>(gu, s);
+        err = launch_gemm<64, 128, 1, 4, true, true, 128>(gu, s);
     else
         err = launch_gemm_dma<true, true>(gu, s);
     if (err != hipSuccess) return err;
     FfnArgs dn{P, p.T, p.k, p.E, p.I, p.H, h, nullptr, offsets, w_down, nullptr, y, s_down,
                nullptr};
     dn.stream_out = P * static_cast<int64_t>(p.H) * 4 > kStreamBytes;
-    if (rows_per_expert <= 24 && p.H % 128 == 0) return launch_gemm<16, 128, 1, 4, false, true>(dn, s);
-    if (rows_per_expert <= 96 || p.H % 256 != 0 || p.I % 128 != 0)
+    if (rows_per_expert <= 24 && p.I % 128 == 0) return launch_gemm<16, 64, 1, 4, false, true, 128>(dn, s);
+    if (rows_per_expert <= 96 || p.H % 256 != 0 || p.I % 128 != 0) {
+        if (p.I % 128 == 0) return launch_gemm<64, 128, 1, 4, false, true, 128>(dn, s);
         return launch_gemm<64, 128, 1, 4, false, true>(dn, s);
+    }
     return launch_gemm_dma<false, true>(dn, s);
 }
 

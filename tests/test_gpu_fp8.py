@@ -49,6 +49,7 @@ SMALL = [
     (600, 512, 256, 16, 4, 2, 4),     # ~150 rows per expert: large tiles, ragged tails
     (33, 384, 192, 32, 4, 2, 6),
     (300, 256, 192, 8, 2, 1, 2),      # ~75 rows per expert: 64-row tiles
+    (300, 256, 256, 8, 2, 1, 2),      # 64-row tiles, both reductions in stages of 128
 ]
 
 
