@@ -217,6 +217,84 @@ def run_dense(steps, warmup):
                          "algorithmic_bytes": bytes_, "algorithmic_flops": flops}}
 
 
+def gemm_study(weights, steps, warmup):
+    """Where the time of the prefill expert GEMMs goes: gate_up and down of
+    the prefill workload (T=8192) with the routed row counts and with
+    hand-made expert_offsets giving every expert the same R rows (R <= 256,
+    one row tile per expert and column tile), next to the library's batched
+    GEMM (torch.bmm, hipBLASLt) on the uniform 256-row shapes.  Events on the
+    current stream; prints one JSON line."""
+    import torch
+
+    from group_limited_routing_router_amd import moe
+    from group_limited_routing_router_amd.inputs import CONFIGS, make_tokens
+
+    cfg = CONFIGS["prefill"]
+    d = make_tokens(cfg, seed=0, device="cuda")
+    d.update(weights)
+    p = moe.MoEProblem.from_config(cfg)
+    b = moe.alloc_buffers(p)
+    moe.moe_route(p, d["x"], d["w_router"], d["bias"], b["topk_ids"], b["topk_weights"])
+    moe.moe_permute(p, b["topk_ids"], b["expert_offsets"], b["sorted_pairs"], b["pair_rows"],
+                    b["ws"])
+    routed = b["expert_offsets"].clone()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    H, I, E = cfg.H, cfg.I, cfg.E
+    rows = {}
+    for name in ["routed", 32, 64, 128, 192, 256]:
+        if name == "routed":
+            b["expert_offsets"].copy_(routed)
+        else:  # every expert takes R of the sorted pairs (each a valid token)
+            b["expert_offsets"].copy_(torch.arange(E + 1, dtype=torch.int32, device="cuda") * name)
+        n = int(b["expert_offsets"][-1])
+        gu = timed(lambda: moe.moe_expert_gate_up(p, d["x"], b["sorted_pairs"], b["expert_offsets"],
+                                                  d["w_gate"], d["w_up"], b["h"]))
+        dn = timed(lambda: moe.moe_expert_down(p, b["h"], b["expert_offsets"], d["w_down"], b["y"]))
+        rows[str(name)] = {"pairs": n, "gate_up_ms": round(gu, 4), "down_ms": round(dn, 4),
+                           "gate_up_mfma_frac": round(4 * n * H * I / (gu * 1e-3) / PEAK_BF16, 4),
+                           "down_mfma_frac": round(2 * n * H * I / (dn * 1e-3) / PEAK_BF16, 4)}
+        log("[study] rows %s: %s" % (name, rows[str(name)]))
+    b["expert_offsets"].copy_(routed)
+    del b, d
+    torch.cuda.empty_cache()
+    # the library on the same uniform shapes: [E, 256, H] x [E, H, 2I] (gate
+    # and up side by side) and [E, 256, I] x [E, I, H], bf16 out, contiguous
+    M = 256
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.empty(E, M, H, dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    w = torch.empty(E, H, 2 * I, dtype=torch.bfloat16, device="cuda").normal_(0, 0.02, generator=g)
+    o = torch.empty(E, M, 2 * I, dtype=torch.bfloat16, device="cuda")
+    t_gu = timed(lambda: torch.bmm(a, w, out=o))
+    del a, w, o
+    a = torch.empty(E, M, I, dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+    w = torch.empty(E, I, H, dtype=torch.bfloat16, device="cuda").normal_(0, 0.02, generator=g)
+    o = torch.empty(E, M, H, dtype=torch.bfloat16, device="cuda")
+    t_dn = timed(lambda: torch.bmm(a, w, out=o))
+    del a, w, o
+    torch.cuda.empty_cache()
+    n = E * M
+    lib = {"gate_up_ms": round(t_gu, 4), "down_ms": round(t_dn, 4),
+           "gate_up_mfma_frac": round(4 * n * H * I / (t_gu * 1e-3) / PEAK_BF16, 4),
+           "down_mfma_frac": round(2 * n * H * I / (t_dn * 1e-3) / PEAK_BF16, 4),
+           "note": "torch.bmm bf16 out, contiguous operands, no gather, no SwiGLU"}
+    log("[study] library bmm, 256 rows per expert: %s" % lib)
+    print(json.dumps({"study": "prefill expert GEMMs by rows per expert",
+                      "workload": "beam-moe-prefill", "steps": steps, "warmup": warmup,
+                      "rows_per_expert": rows, "library_bmm_256_rows": lib}), flush=True)
+
+
 def roofline_for(res, kernel):
     c = res["counts"][kernel]
     ms = res["kernel_ms"][kernel]
@@ -321,6 +399,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--gemm-study", action="store_true",
+                    help="instead of the benchmark: the prefill expert GEMMs at fixed rows per "
+                         "expert next to the library batched GEMM (one JSON line)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -338,6 +419,9 @@ def main():
     moe.load_library()
     weights = make_weights(CONFIGS["decode"], seed=0, device="cuda")
     torch.cuda.synchronize()
+    if args.gemm_study:
+        gemm_study(weights, args.steps, args.warmup)
+        return
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
