@@ -16,8 +16,8 @@
 // a lane holds gate and up accumulators of the same (row, col) and the SwiGLU
 // epilogue needs no data exchange.
 //   ffn_gemm_kernel      16- or 64-row tiles (few rows per expert: decode),
-//                        16x16x32 MFMA, K staged 64 at a time through two
-//                        padded LDS buffers via registers.
+//                        16x16x32 MFMA, K staged 64 or 128 at a time through
+//                        two padded LDS buffers via registers.
 //   ffn_gemm_dma_kernel  256 x 256 tiles (many rows per expert: prefill),
 //                        32x32x16 MFMA, operands loaded straight into LDS.
 //
