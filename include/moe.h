@@ -19,7 +19,10 @@
  *    row-major and 16-byte aligned.  bf16 tensors are passed as moe_bf16 (the
  *    raw 16-bit pattern).
  *  - The library never allocates, frees or synchronises; each call only
- *    enqueues kernels on `stream` (0 = the null stream).
+ *    enqueues kernels on `stream` (0 = the null stream).  No call reads
+ *    results back to the host or clears memory with a memset, so a call can
+ *    be captured into a HIP graph and replayed (the tile schedule of the
+ *    expert GEMMs is derived on the device from expert_offsets).
  *  - Every argument is checked on the host before anything is enqueued.  On
  *    any error nothing is enqueued and no output is touched; the call returns
  *    a moe_status and moe_last_error() gives a message (per host thread).

@@ -1,0 +1,74 @@
+"""The forward pass only enqueues work on the caller's stream (no allocation,
+no synchronisation, no host read-back, no memset), so it can be captured into
+a HIP graph: each replay must reproduce the eager call bit for bit.  The graph
+is replayed several times with eager work and synchronisations in between,
+and every replay is checked."""
+import pytest
+import torch
+
+from group_limited_routing_router_amd.inputs import MoEConfig, make_inputs, make_weights_fp8
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    from group_limited_routing_router_amd import moe as m
+    m.load_library()
+    return m
+
+
+CASES = [
+    # (T, H, I, E, G, TG, k): 16-row tiles; large tiles with ragged tails
+    (64, 256, 128, 16, 4, 2, 4),
+    (600, 512, 256, 16, 4, 2, 4),
+]
+
+
+@pytest.mark.parametrize("shape", CASES, ids=lambda s: "T%d_H%d_I%d_E%d_k%d" % (s[0], s[1], s[2], s[3], s[6]))
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16", "fp8"])
+def test_forward_replays_from_a_graph(moe, shape, fp8):
+    T, H, I, E, G, TG, k = shape
+    print(f"[case] graph fp8={fp8} T={T} H={H} I={I} E={E} k={k}", flush=True)
+    cfg = MoEConfig("graph", T=T, H=H, I=I, E=E, G=G, TG=TG, k=k, scale=2.5)
+    d = {n: v.cuda() for n, v in make_inputs(cfg, seed=5).items()}
+    w8 = make_weights_fp8(cfg, seed=5, device="cuda") if fp8 else None
+    p = moe.MoEProblem.from_config(cfg)
+    b = moe.alloc_buffers(p)
+
+    def forward():
+        if fp8:
+            moe.moe_forward_fp8(p, d["x"], w8["w_router"], d["bias"], w8["q_gate"], w8["s_gate"],
+                                w8["q_up"], w8["s_up"], w8["q_down"], w8["s_down"], b["out"],
+                                b["topk_ids"], b["topk_weights"], b["y"], b["ws"])
+        else:
+            moe.moe_forward(p, d["x"], d["w_router"], d["bias"], d["w_gate"], d["w_up"],
+                            d["w_down"], b["out"], b["topk_ids"], b["topk_weights"], b["y"], b["ws"])
+
+    forward()
+    torch.cuda.synchronize()
+    ref = {n: b[n].clone() for n in ("out", "topk_ids", "topk_weights", "y")}
+
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            forward()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+
+    for replay in range(3):
+        for n in ref:  # eager work between replays: clear every output
+            b[n].zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in ref:
+            assert torch.equal(b[n], ref[n]), f"replay {replay}: {n} differs from the eager call"
+        # eager work on the same buffers after a replay
+        forward()
+        torch.cuda.synchronize()
+        assert torch.equal(b["out"], ref["out"])
+    del graph
