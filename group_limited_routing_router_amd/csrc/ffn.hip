@@ -403,10 +403,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
 }
 
-// FP8 = true: the weights are E4M3 codes (64 bytes a row and stage, 16 rows
-// per 1-KB load, 16-byte chunk c of row r at c ^ ((r >> 2) & 3)), widened to
-// bf16 as each MFMA operand is read; the per-channel scale multiplies the
-// accumulators before the results are stored.
+// FP8 = true: the weights are E4M3 codes, widened to bf16 as each MFMA
+// operand is read; the per-channel scale multiplies the accumulators before
+// the results are stored.  A weight stage then spans two activation stages
+// (K = 128 codes, again 128 bytes a row: every weight row of a stage is one
+// whole line, laid out and swizzled like an activation row), and its loads
+// are spread over those two.
 template <bool GATEUP, bool FP8 = false>
 __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
     constexpr int BM = 256, BN = 256, WAVES_M = 2, WAVES_N = 2;
@@ -418,16 +420,19 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
     constexpr int NFB = NACC * NB;             // B fragments per substep (4)
     constexpr int ROW_BYTES = BK * 2;          // 128 (activations)
     constexpr int EB = FP8 ? 1 : 2;            // bytes per weight
-    constexpr int B_ROW = BK * EB;             // 128 or 64 (weights)
+    constexpr int SB = FP8 ? 2 : 1;            // activation stages per weight stage
+    constexpr int B_ROW = BK * SB * EB;        // 128 bytes of each weight row per weight stage
+    static_assert(B_ROW == ROW_BYTES, "weight rows are staged like activation rows");
     constexpr int A_STAGE = BM * ROW_BYTES;    // 32 KB
-    constexpr int B_STAGE = BN * B_ROW;        // 32 or 16 KB
+    constexpr int B_STAGE = BN * B_ROW;        // 32 KB
     constexpr int A_BUFS = 2, B_BUFS = 3;
     constexpr int ARENA = A_BUFS * A_STAGE + B_BUFS * B_STAGE;
     static_assert(ARENA <= kDmaArena, "LDS budget");
     constexpr int DMA_A = BM / kWaves / 8;     // 1-KB activation loads per wave and stage (8)
-    constexpr int B_RPL = 1024 / B_ROW;        // weight rows per 1-KB load (8 or 16)
-    constexpr int B_LPR = B_ROW / 16;          // lanes per weight row (8 or 4)
-    constexpr int DMA_B = BN / kWaves / B_RPL; // weight loads per wave and stage (8 or 4)
+    constexpr int B_RPL = 1024 / B_ROW;        // weight rows per 1-KB load (8)
+    constexpr int B_LPR = B_ROW / 16;          // lanes per weight row (8)
+    constexpr int DMA_BS = BN / kWaves / B_RPL; // weight loads per wave and weight stage (8)
+    constexpr int DMA_B = DMA_BS / SB;         // ... per activation stage (8, FP8: 4)
 
     __shared__ __attribute__((aligned(1024))) unsigned char s_arena[ARENA];
     const uint32_t arena = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(s_arena));
@@ -452,7 +457,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
     // chunk L % 8, i.e. logical chunk (L % 8) ^ ((row >> 1) & 7). ----
     constexpr uint32_t kOutside = 0x80000000u;
     __amdgpu_buffer_rsrc_t rsrc_a, rsrc_b;
-    uint32_t va[DMA_A], vb[DMA_B];
+    uint32_t va[DMA_A], vb[DMA_BS];
     if constexpr (GATEUP)
         rsrc_a = make_rsrc(a.a_src, static_cast<uint32_t>(a.T * K * 2));
     else
@@ -485,9 +490,9 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
         va[j] = av;
     }
 #pragma unroll
-    for (int j = 0; j < DMA_B; ++j) {
+    for (int j = 0; j < DMA_BS; ++j) {
         const int r = wave * 64 + j * B_RPL + lane / B_LPR;
-        const int c = FP8 ? ((lane % B_LPR) ^ ((r >> 2) & 3)) : ((lane % B_LPR) ^ ((r >> 1) & 7));
+        const int c = (lane % B_LPR) ^ ((r >> 1) & 7);
         const int rb = GATEUP ? (r & (BN_OUT - 1)) : r;  // row within the gate / up half
         vb[j] = static_cast<uint32_t>(rb * K * EB + c * 16);
     }
@@ -497,9 +502,9 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
         dma_load16(a_buf(buf) + (wave * 64 + j * 8) * ROW_BYTES, rsrc_a, va[j],
                    static_cast<uint32_t>(kt * ROW_BYTES));
     };
-    auto dma_b = [&](int j, int buf, int kt) {
+    auto dma_b = [&](int j, int buf, int kbs) {  // load j of weight stage kbs
         dma_load16(b_buf(buf) + (wave * 64 + j * B_RPL) * B_ROW, rsrc_b, vb[j],
-                   static_cast<uint32_t>(kt * B_ROW));
+                   static_cast<uint32_t>(kbs * B_ROW));
     };
 
     const int wm = wave / WAVES_N, wn = wave % WAVES_N;
@@ -535,7 +540,8 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
             BFrag b[NFB];
         };
         // piece q of substep ks's fragments: A blocks first, then B blocks
-        auto load_piece = [&](Frags& f, int ab, int bb, int ks, auto qc) {
+        // (FP8: from half hb of the weight stage)
+        auto load_piece = [&](Frags& f, int ab, int bb, int ks, int hb, auto qc) {
             constexpr int q = decltype(qc)::value;
             const int c = ks * 2 + half;
             if constexpr (q < NV) {
@@ -547,17 +553,16 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
                 const unsigned char* sb = s_arena + (b_buf(bb) - arena);
                 const int br = g * BN_OUT + wn * WN_OUT + n * 32 + r32;
                 if constexpr (FP8) {
-                    // 8 codes: 8-byte half (c & 1) of chunk (c >> 1)
-                    f.b[gn] = *reinterpret_cast<const u32x2*>(
-                        sb + br * B_ROW + ((((c >> 1) ^ ((br >> 2) & 3))) << 4) + ((c & 1) << 3));
+                    // 8 codes: 8-byte half `half` of 16-byte chunk 4 hb + ks
+                    f.b[gn] = *reinterpret_cast<const u32x2*>(sb + frag_off(br, hb * 4 + ks) + (half << 3));
                 } else {
                     f.b[gn] = *reinterpret_cast<const bf16x8*>(sb + frag_off(br, c));
                 }
             }
         };
         constexpr int NP = NV > 0 ? NV + NFB : 0;  // fragment pieces per substep
-        auto load_frags = [&](Frags& f, int ab, int bb, int ks) {
-            static_for<0, NP>([&](auto qc) { load_piece(f, ab, bb, ks, qc); });
+        auto load_frags = [&](Frags& f, int ab, int bb, int ks, int hb) {
+            static_for<0, NP>([&](auto qc) { load_piece(f, ab, bb, ks, hb, qc); });
         };
         // MFMA i = (g * NB + n) * NV + m of a substep; bop holds B fragment gn
         // in bf16 (FIRST: MFMA i is the first of a run on it, so it is
@@ -577,24 +582,29 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
                 acc[g][m][n] = mfma32(f.a[m], bop, acc[g][m][n]);
             }
         };
-        const int nk = K / BK;
+        const int nk = K / BK;     // activation stages (a multiple of SB)
+        const int nbs = nk / SB;   // weight stages
         // prologue: A(0), B(0), B(1) in flight; wait for the first two
 #pragma unroll
         for (int j = 0; j < DMA_A; ++j) dma_a(j, 0, 0);
 #pragma unroll
-        for (int j = 0; j < DMA_B; ++j) dma_b(j, 0, 0);
+        for (int j = 0; j < DMA_BS; ++j) dma_b(j, 0, 0);
 #pragma unroll
-        for (int j = 0; j < DMA_B; ++j) dma_b(j, 1, nk > 1 ? 1 : 0);
-        wait_vmcnt<DMA_B>();
+        for (int j = 0; j < DMA_BS; ++j) dma_b(j, 1, nbs > 1 ? 1 : 0);
+        wait_vmcnt<DMA_BS>();
         __syncthreads();
         int abuf = 0, bbuf = 0;
         Frags f0, f1;
-        load_frags(f0, 0, 0, 0);
-        for (int kt = 0; kt < nk; ++kt) {
-            const int ka = kt + 1 < nk ? kt + 1 : nk - 1;   // past the end: refill an idle buffer
-            const int kb = kt + 2 < nk ? kt + 2 : nk - 1;
+        load_frags(f0, 0, 0, 0, 0);
+        // activation stage kt = kt0 + HB is half HB of weight stage kt0 / SB
+        for (int kt0 = 0; kt0 < nk; kt0 += SB) static_for<0, SB>([&](auto hb_c) {
+            constexpr int HB = decltype(hb_c)::value;
+            const int kt = kt0 + HB;
+            const int kbs = kt0 / SB;
+            const int ka = kt + 1 < nk ? kt + 1 : nk - 1;      // past the end: refill an idle buffer
+            const int kb = kbs + 2 < nbs ? kbs + 2 : nbs - 1;  // weight stage loaded two ahead
             const int anext = abuf ^ 1;
-            const int bnext = bbuf == 0 ? 2 : bbuf - 1;     // (bbuf + 2) % 3
+            const int bnext = bbuf == 0 ? 2 : bbuf - 1;        // (bbuf + 2) % 3
             // Phases are pinned with scheduling fences (the compiler would
             // otherwise sink fragment reads next to their MFMAs or bunch them):
             // the fragments of the next substep are read one at a time between
@@ -626,7 +636,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
                     constexpr int i = decltype(ic)::value;
                     static_for<0, NPC>([&](auto qc) {
                         constexpr int q = decltype(qc)::value;
-                        if constexpr (q * IT / (NPC > 0 ? NPC : 1) == i) load_piece(fn, abuf, bbuf, KN, qc);
+                        if constexpr (q * IT / (NPC > 0 ? NPC : 1) == i) load_piece(fn, abuf, bbuf, KN, HB, qc);
                     });
                     if constexpr (i < NM) mfma_one(f, std::integral_constant<int, LO + i>{}, bop, i == 0);
                     constexpr int step = NM >= NL ? (NL > 0 ? NM / NL : 1) : 1;
@@ -635,7 +645,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
                         if constexpr (j < DMA_A)
                             dma_a(j, anext, ka);
                         else
-                            dma_b(j - DMA_A, bnext, kb);
+                            dma_b(HB * DMA_B + j - DMA_A, bnext, kb);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 });
@@ -651,11 +661,11 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
             wait_vmcnt<DMA_B>();
             __syncthreads();
             abuf = anext;
-            bbuf = bbuf == 2 ? 0 : bbuf + 1;
-            load_frags(f0, abuf, bbuf, 0);  // after the last stage: read, never used
+            if constexpr (HB == SB - 1) bbuf = bbuf == 2 ? 0 : bbuf + 1;
+            load_frags(f0, abuf, bbuf, 0, (HB + 1) % SB);  // after the last stage: read, never used
             __builtin_amdgcn_sched_barrier(0);
             substep(f1, std::integral_constant<int, -1>{}, CH{}, CM{}, f0, KNone{});
-        }
+        });
         wait_vmcnt<0>();
         __syncthreads();
     };
