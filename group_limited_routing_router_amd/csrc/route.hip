@@ -8,7 +8,8 @@
 // router runs in FP32 (same page, section "Residual Stream").  Ties go to the
 // lower index.
 //
-// One workgroup owns up to 16*MB tokens and all E <= 256 experts.  The
+// route_kernel (batches above 512 tokens): one workgroup owns up to 16*MB
+// tokens and all E <= 256 experts.  The
 // logits x . w_router^T are a small dense contraction with bf16 inputs and
 // fp32 accumulation, so they run on 16x16x32 bf16 MFMA.  The hidden dimension
 // is walked 64 at a time: the workgroup loads the router-weight tile (256
@@ -20,6 +21,10 @@
 // the steps in order.  Scores never leave LDS: group ranking and the top-k
 // run in the same kernel, one wave per token, with the k picks done as k
 // wave-wide arg-max reductions.
+//
+// route_small_kernel (up to 512 tokens): one workgroup per token or two,
+// logits as per-lane bf16 dot products over register-held token chunks and
+// a butterfly sum over the wave (see the kernel); the same selection.
 #include "common.h"
 #include "kernels.h"
 
@@ -35,6 +40,107 @@ constexpr int kWTile = kMaxE * kRowBytes;  // router-weight tile of one step (32
 // XOR-swizzled so the 16 rows of one MFMA operand read hit distinct banks.
 __device__ __forceinline__ int stage_off(int r, int c) {
     return r * kRowBytes + ((c ^ ((r >> 1) & 7)) << 4);
+}
+
+// Group-limited top-k of the scores of TT tokens in LDS (rows of s_score; row
+// tt is token tok0 + tt, rows at or past tpw or T are ignored): group score =
+// sum of the group's two best scores, the TG best groups kept (ties to the
+// lower index), then one wave per token picks the k best experts of the kept
+// groups as k wave-wide arg-max reductions (ties to the lower index) and
+// writes ids and weights (the scores normalised to sum to one).  s_gscore and
+// s_kept are LDS scratch; NT threads take part, all of them must call.
+template <int TT, int NT>
+__device__ __forceinline__ void select_topk(float (*s_score)[kMaxE + 4], float (*s_gscore)[kMaxE],
+                                            unsigned char (*s_kept)[kMaxE], int64_t tok0, int tpw,
+                                            int64_t T, int E, int G, int TG, int k,
+                                            int32_t* __restrict__ ids, float* __restrict__ weights) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // ---- group scores: sum of each group's two best scores ----
+    const int gs = E / G;
+    for (int item = tid; item < TT * G; item += NT) {
+        const int tt = item / G, g = item - tt * G;
+        const float* s = &s_score[tt][g * gs];
+        float t1 = s[0], t2 = -1.0f;
+        for (int i = 1; i < gs; ++i) {
+            const float v = s[i];
+            if (v > t1) {
+                t2 = t1;
+                t1 = v;
+            } else if (v > t2) {
+                t2 = v;
+            }
+        }
+        s_gscore[tt][g] = gs == 1 ? t1 : t1 + t2;
+    }
+    __syncthreads();
+    // ---- kept groups: rank under (score desc, index asc) below TG ----
+    for (int item = tid; item < TT * G; item += NT) {
+        const int tt = item / G, g = item - tt * G;
+        const float mine = s_gscore[tt][g];
+        int rank = 0;
+        for (int o = 0; o < G; ++o) {
+            const float v = s_gscore[tt][o];
+            rank += (v > mine) || (v == mine && o < g);
+        }
+        s_kept[tt][g] = rank < TG;
+    }
+    __syncthreads();
+
+    // ---- top-k among kept groups: one wave per token ----
+    for (int tt = wave; tt < tpw; tt += NT / kWave) {
+        const int64_t t = tok0 + tt;
+        if (t >= T) break;  // wave-uniform; no barrier follows
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane + 64 * i;
+            v[i] = (e < E && s_kept[tt][e / gs]) ? s_score[tt][e] : -1.0f;
+        }
+        float pick_v[kMaxK];
+        int pick_e[kMaxK];
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j >= k) break;
+            float bv = v[0];
+            int be = lane;
+#pragma unroll
+            for (int i = 1; i < 4; ++i)
+                if (v[i] > bv) {
+                    bv = v[i];
+                    be = lane + 64 * i;
+                }
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) {
+                const float ov = __shfl_xor(bv, off);
+                const int oe = __shfl_xor(be, off);
+                if (ov > bv || (ov == bv && oe < be)) {
+                    bv = ov;
+                    be = oe;
+                }
+            }
+            pick_v[j] = bv;
+            pick_e[j] = be;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (lane + 64 * i == be) v[i] = -2.0f;
+        }
+        float sum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j >= k) break;
+            sum = sum + pick_v[j];
+        }
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) {
+            if (j >= k) break;
+            if (lane == j) {
+                ids[t * k + j] = pick_e[j];
+                weights[t * k + j] = pick_v[j] / sum;
+            }
+        }
+    }
 }
 
 // NW waves; a workgroup owns tpw <= TT = 16 * MB tokens (with few tokens a
@@ -172,97 +278,120 @@ __global__ __launch_bounds__(64 * NW) void route_kernel(
     }
     __syncthreads();
 
-    // ---- group scores: sum of each group's two best scores ----
-    const int gs = E / G;
-    for (int item = tid; item < TT * G; item += NT) {
-        const int tt = item / G, g = item - tt * G;
-        const float* s = &s_score[tt][g * gs];
-        float t1 = s[0], t2 = -1.0f;
-        for (int i = 1; i < gs; ++i) {
-            const float v = s[i];
-            if (v > t1) {
-                t2 = t1;
-                t1 = v;
-            } else if (v > t2) {
-                t2 = v;
-            }
-        }
-        s_gscore[tt][g] = gs == 1 ? t1 : t1 + t2;
-    }
-    __syncthreads();
-    // ---- kept groups: rank under (score desc, index asc) below TG ----
-    for (int item = tid; item < TT * G; item += NT) {
-        const int tt = item / G, g = item - tt * G;
-        const float mine = s_gscore[tt][g];
-        int rank = 0;
-        for (int o = 0; o < G; ++o) {
-            const float v = s_gscore[tt][o];
-            rank += (v > mine) || (v == mine && o < g);
-        }
-        s_kept[tt][g] = rank < TG;
-    }
-    __syncthreads();
+    select_topk<TT, NT>(s_score, s_gscore, s_kept, tok0, tpw, T, E, G, TG, k, ids, weights);
+}
 
-    // ---- top-k among kept groups: one wave per token ----
-    for (int tt = wave; tt < tpw; tt += NT / kWave) {
-        const int64_t t = tok0 + tt;
-        if (t >= T) break;  // wave-uniform; no barrier follows
-        float v[4];
+// Few tokens (decode batches): a workgroup owns TPW tokens and all experts,
+// without MFMA (one token would fill one of its sixteen rows) and without LDS
+// staging.  Lane l of every wave holds the tokens' 16-byte hidden chunks l,
+// l + 64, ... (8 values each, XC chunks) in registers.  Wave w takes experts
+// w, w + NW, ...: it reads an expert's router row as whole 1-KB pieces (lane l
+// reads chunk l of each piece), accumulates the bf16 products of its chunks
+// in fp32 with two-wide dot instructions in chunk order, and sums the 64 lane
+// partials with a butterfly (every lane ends with the same sum).  Then bias,
+// sigmoid and select_topk as in route_kernel.
+template <int NW, int TPW, int XC>
+__global__ __launch_bounds__(64 * NW) void route_small_kernel(
+    int64_t T, int H, int E, int G, int TG, int k, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ wr, const float* __restrict__ bias, int32_t* __restrict__ ids,
+    float* __restrict__ weights) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    __shared__ float s_score[TPW][kMaxE + 4];
+    __shared__ float s_gscore[TPW][kMaxE];
+    __shared__ unsigned char s_kept[TPW][kMaxE];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * TPW;
+    const int nch = H >> 3;  // 16-byte chunks per row (<= 64 XC)
+
+    u32x4 xr[TPW][XC];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int e = lane + 64 * i;
-            v[i] = (e < E && s_kept[tt][e / gs]) ? s_score[tt][e] : -1.0f;
-        }
-        float pick_v[kMaxK];
-        int pick_e[kMaxK];
+    for (int t = 0; t < TPW; ++t) {
+        int64_t tok = tok0 + t;
+        if (tok > T - 1) tok = T - 1;  // rows past the batch repeat its last token; dropped
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            if (j >= k) break;
-            float bv = v[0];
-            int be = lane;
-#pragma unroll
-            for (int i = 1; i < 4; ++i)
-                if (v[i] > bv) {
-                    bv = v[i];
-                    be = lane + 64 * i;
-                }
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off);
-                const int oe = __shfl_xor(be, off);
-                if (ov > bv || (ov == bv && oe < be)) {
-                    bv = ov;
-                    be = oe;
-                }
-            }
-            pick_v[j] = bv;
-            pick_e[j] = be;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (lane + 64 * i == be) v[i] = -2.0f;
-        }
-        float sum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            if (j >= k) break;
-            sum = sum + pick_v[j];
-        }
-#pragma unroll
-        for (int j = 0; j < kMaxK; ++j) {
-            if (j >= k) break;
-            if (lane == j) {
-                ids[t * k + j] = pick_e[j];
-                weights[t * k + j] = pick_v[j] / sum;
-            }
+        for (int i = 0; i < XC; ++i) {
+            const int c = i * 64 + lane;
+            xr[t][i] = c < nch ? ld16(x + tok * H + c * 8) : u32x4{0u, 0u, 0u, 0u};
         }
     }
+    auto dot8 = [&](const u32x4& a, const u32x4& b, float acc) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // elements copied out first: a bit cast of a vector element in
+            // place would read element 0
+            const uint32_t aj = a[j], bj = b[j];
+            acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, aj),
+                                                  __builtin_bit_cast(bf16x2, bj), acc, false);
+        }
+        return acc;
+    };
+    // FULL: every lane has all XC chunks (H = 512 XC), no per-lane guards
+    auto experts = [&](auto full_c) {
+        constexpr bool FULL = decltype(full_c)::value;
+#pragma unroll 2
+        for (int e = wave; e < E; e += NW) {
+            const uint16_t* row = wr + static_cast<int64_t>(e) * H;
+            u32x4 w[XC];
+#pragma unroll
+            for (int i = 0; i < XC; ++i) {
+                const int c = i * 64 + lane;
+                w[i] = (FULL || c < nch) ? ld16(row + c * 8) : u32x4{0u, 0u, 0u, 0u};
+            }
+            float acc[TPW];
+#pragma unroll
+            for (int t = 0; t < TPW; ++t) {
+                acc[t] = 0.0f;
+#pragma unroll
+                for (int i = 0; i < XC; ++i) acc[t] = dot8(xr[t][i], w[i], acc[t]);
+#pragma unroll
+                for (int off = 32; off >= 1; off >>= 1) acc[t] = acc[t] + __shfl_xor(acc[t], off);
+            }
+            if (lane == 0) {
+                const float be = bias ? bias[e] : 0.0f;
+#pragma unroll
+                for (int t = 0; t < TPW; ++t) s_score[t][e] = sigmoid_f32(acc[t] + be);
+            }
+        }
+    };
+    if (nch == 64 * XC)
+        experts(std::true_type{});
+    else
+        experts(std::false_type{});
+    __syncthreads();
+    select_topk<TPW, 64 * NW>(s_score, s_gscore, s_kept, tok0, TPW, T, E, G, TG, k, ids, weights);
+}
+
+template <int TPW, int XC>
+void launch_route_small(const Problem& p, const uint16_t* x, const uint16_t* w_router,
+                        const float* bias, int32_t* ids, float* weights, hipStream_t s) {
+    const int64_t grid = (p.T + TPW - 1) / TPW;
+    route_small_kernel<8, TPW, XC><<<dim3(static_cast<unsigned>(grid)), dim3(512), 0, s>>>(
+        p.T, p.H, p.E, p.G, p.TG, p.k, x, w_router, bias, ids, weights);
 }
 
 }  // namespace
 
 hipError_t launch_route(const Problem& p, const uint16_t* x, const uint16_t* w_router,
                         const float* bias, int32_t* ids, float* weights, hipStream_t s) {
-    if (p.T >= 4096) {
+    const int xc = (p.H / 8 + 63) / 64;  // hidden chunks per lane of the small-batch kernel
+    if (p.T <= 512 && xc <= 16) {
+        // few tokens: one or two per workgroup, at most 256 workgroups
+        if (p.T <= 256) {
+            if (xc <= 1) launch_route_small<1, 1>(p, x, w_router, bias, ids, weights, s);
+            else if (xc <= 2) launch_route_small<1, 2>(p, x, w_router, bias, ids, weights, s);
+            else if (xc <= 4) launch_route_small<1, 4>(p, x, w_router, bias, ids, weights, s);
+            else if (xc <= 10) launch_route_small<1, 10>(p, x, w_router, bias, ids, weights, s);
+            else launch_route_small<1, 16>(p, x, w_router, bias, ids, weights, s);
+        } else {
+            if (xc <= 1) launch_route_small<2, 1>(p, x, w_router, bias, ids, weights, s);
+            else if (xc <= 2) launch_route_small<2, 2>(p, x, w_router, bias, ids, weights, s);
+            else if (xc <= 4) launch_route_small<2, 4>(p, x, w_router, bias, ids, weights, s);
+            else if (xc <= 10) launch_route_small<2, 10>(p, x, w_router, bias, ids, weights, s);
+            else launch_route_small<2, 16>(p, x, w_router, bias, ids, weights, s);
+        }
+    } else if (p.T >= 4096) {
         // many tokens: 32-token tiles (the router weight is read once per tile)
         const int64_t grid = (p.T + 31) / 32;
         route_kernel<2, 8, 6><<<dim3(static_cast<unsigned>(grid)), dim3(512), 0, s>>>(
