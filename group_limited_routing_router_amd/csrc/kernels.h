@@ -22,6 +22,14 @@ inline int64_t permute_blocks(int64_t pairs) {
 hipError_t launch_route(const Problem& p, const uint16_t* x, const uint16_t* w_router,
                         const float* bias, int32_t* ids, float* weights, hipStream_t s);
 
+// The router with device scratch of at least T*E*4 bytes (unused contents):
+// for up to 512 tokens the experts are split over workgroups and the scores
+// pass through the scratch (the same scores, bit for bit, as launch_route);
+// otherwise, or with too little scratch, launch_route.
+hipError_t launch_route_scratch(const Problem& p, const uint16_t* x, const uint16_t* w_router,
+                                const float* bias, int32_t* ids, float* weights, void* scratch,
+                                size_t scratch_bytes, hipStream_t s);
+
 hipError_t launch_permute(const Problem& p, const int32_t* ids, int32_t* offsets,
                           int32_t* sorted_pairs, int32_t* pair_rows, int32_t* block_counts,
                           hipStream_t s);

@@ -338,7 +338,12 @@ MOE_EXPORT moe_status moe_forward_fp8(const moe_problem* p, const moe_bf16* x,
     int32_t* off = at<int32_t>(ws, L.offsets);
     int32_t* sorted = at<int32_t>(ws, L.sorted);
     int32_t* rows = at<int32_t>(ws, L.rows);
-    hipError_t e = moe::launch_route(q, x, w_router, bias, ids, wts, stream);
+    // the h region is written only by the expert step, after routing: it
+    // doubles as the router's score scratch
+    const size_t h_bytes = static_cast<size_t>(p->T) * static_cast<size_t>(p->k) *
+                           static_cast<size_t>(p->I) * 2;
+    hipError_t e = moe::launch_route_scratch(q, x, w_router, bias, ids, wts, at<uint16_t>(ws, L.h),
+                                             h_bytes, stream);
     if (e != hipSuccess) return hip_status(e, "route launch");
     e = moe::launch_permute(q, ids, off, sorted, rows, at<int32_t>(ws, L.counts), stream);
     if (e != hipSuccess) return hip_status(e, "permute launch");
@@ -377,7 +382,12 @@ MOE_EXPORT moe_status moe_forward(const moe_problem* p, const moe_bf16* x,
     int32_t* off = at<int32_t>(ws, L.offsets);
     int32_t* sorted = at<int32_t>(ws, L.sorted);
     int32_t* rows = at<int32_t>(ws, L.rows);
-    hipError_t e = moe::launch_route(q, x, w_router, bias, ids, wts, stream);
+    // the h region is written only by the expert step, after routing: it
+    // doubles as the router's score scratch
+    const size_t h_bytes = static_cast<size_t>(p->T) * static_cast<size_t>(p->k) *
+                           static_cast<size_t>(p->I) * 2;
+    hipError_t e = moe::launch_route_scratch(q, x, w_router, bias, ids, wts, at<uint16_t>(ws, L.h),
+                                             h_bytes, stream);
     if (e != hipSuccess) return hip_status(e, "route launch");
     e = moe::launch_permute(q, ids, off, sorted, rows, at<int32_t>(ws, L.counts), stream);
     if (e != hipSuccess) return hip_status(e, "permute launch");

@@ -281,31 +281,20 @@ __global__ __launch_bounds__(64 * NW) void route_kernel(
     select_topk<TT, NT>(s_score, s_gscore, s_kept, tok0, tpw, T, E, G, TG, k, ids, weights);
 }
 
-// Few tokens (decode batches): a workgroup owns TPW tokens and all experts,
-// without MFMA (one token would fill one of its sixteen rows) and without LDS
-// staging.  Lane l of every wave holds the tokens' 16-byte hidden chunks l,
-// l + 64, ... (8 values each, XC chunks) in registers.  Wave w takes experts
-// w, w + NW, ...: it reads an expert's router row as whole 1-KB pieces (lane l
-// reads chunk l of each piece), accumulates the bf16 products of its chunks
-// in fp32 with two-wide dot instructions in chunk order, and sums the 64 lane
-// partials with a butterfly (every lane ends with the same sum).  Then bias,
-// sigmoid and select_topk as in route_kernel.
-template <int NW, int TPW, int XC>
-__global__ __launch_bounds__(64 * NW) void route_small_kernel(
-    int64_t T, int H, int E, int G, int TG, int k, const uint16_t* __restrict__ x,
-    const uint16_t* __restrict__ wr, const float* __restrict__ bias, int32_t* __restrict__ ids,
-    float* __restrict__ weights) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    __shared__ float s_score[TPW][kMaxE + 4];
-    __shared__ float s_gscore[TPW][kMaxE];
-    __shared__ unsigned char s_kept[TPW][kMaxE];
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * TPW;
-    const int nch = H >> 3;  // 16-byte chunks per row (<= 64 XC)
-
-    u32x4 xr[TPW][XC];
+// Few tokens (decode batches): no MFMA (one token would fill one of its
+// sixteen rows) and no LDS staging.  Lane l of every wave holds the tokens'
+// 16-byte hidden chunks l, l + 64, ... (8 values each, XC chunks) in
+// registers.  Wave w takes experts e_begin + w, e_begin + w + NW, ...: it
+// reads an expert's router row as whole 1-KB pieces (lane l reads chunk l of
+// each piece), accumulates the bf16 products of its chunks in fp32 with
+// two-wide dot instructions in chunk order, and sums the 64 lane partials
+// with a butterfly (every lane ends with the same sum).  Lane 0 hands
+// sigmoid(sum + bias) to out(t, e, score).  Every kernel below computes a
+// score with this one function, so they agree bit for bit.
+template <int TPW, int XC>
+__device__ __forceinline__ void load_token_chunks(u32x4 (&xr)[TPW][XC], const uint16_t* __restrict__ x,
+                                                  int64_t T, int H, int64_t tok0, int lane) {
+    const int nch = H >> 3;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
         int64_t tok = tok0 + t;
@@ -316,6 +305,14 @@ __global__ __launch_bounds__(64 * NW) void route_small_kernel(
             xr[t][i] = c < nch ? ld16(x + tok * H + c * 8) : u32x4{0u, 0u, 0u, 0u};
         }
     }
+}
+
+template <int NW, int TPW, int XC, typename Out>
+__device__ __forceinline__ void small_scores(const u32x4 (&xr)[TPW][XC], const uint16_t* __restrict__ wr,
+                                             const float* __restrict__ bias, int H, int e_begin,
+                                             int e_end, int lane, int wave, Out out) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const int nch = H >> 3;  // 16-byte chunks per row (<= 64 XC)
     auto dot8 = [&](const u32x4& a, const u32x4& b, float acc) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -331,7 +328,7 @@ __global__ __launch_bounds__(64 * NW) void route_small_kernel(
     auto experts = [&](auto full_c) {
         constexpr bool FULL = decltype(full_c)::value;
 #pragma unroll 2
-        for (int e = wave; e < E; e += NW) {
+        for (int e = e_begin + wave; e < e_end; e += NW) {
             const uint16_t* row = wr + static_cast<int64_t>(e) * H;
             u32x4 w[XC];
 #pragma unroll
@@ -351,7 +348,7 @@ __global__ __launch_bounds__(64 * NW) void route_small_kernel(
             if (lane == 0) {
                 const float be = bias ? bias[e] : 0.0f;
 #pragma unroll
-                for (int t = 0; t < TPW; ++t) s_score[t][e] = sigmoid_f32(acc[t] + be);
+                for (int t = 0; t < TPW; ++t) out(t, e, sigmoid_f32(acc[t] + be));
             }
         }
     };
@@ -359,8 +356,79 @@ __global__ __launch_bounds__(64 * NW) void route_small_kernel(
         experts(std::true_type{});
     else
         experts(std::false_type{});
+}
+
+// A workgroup owns TPW tokens and all experts; then select_topk.
+template <int NW, int TPW, int XC>
+__global__ __launch_bounds__(64 * NW) void route_small_kernel(
+    int64_t T, int H, int E, int G, int TG, int k, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ wr, const float* __restrict__ bias, int32_t* __restrict__ ids,
+    float* __restrict__ weights) {
+    __shared__ float s_score[TPW][kMaxE + 4];
+    __shared__ float s_gscore[TPW][kMaxE];
+    __shared__ unsigned char s_kept[TPW][kMaxE];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * TPW;
+    u32x4 xr[TPW][XC];
+    load_token_chunks<TPW, XC>(xr, x, T, H, tok0, lane);
+    small_scores<NW, TPW, XC>(xr, wr, bias, H, 0, E, lane, wave,
+                              [&](int t, int e, float v) { s_score[t][e] = v; });
     __syncthreads();
     select_topk<TPW, 64 * NW>(s_score, s_gscore, s_kept, tok0, TPW, T, E, G, TG, k, ids, weights);
+}
+
+// The same scores with the experts split over workgroups (tokens
+// [TPW blockIdx.x, +TPW), experts [es blockIdx.y, +es)), written to scores
+// [T, E] in memory; route_select_kernel then selects.  Each workgroup reads
+// only its slice of the router weight, once for its TPW tokens.
+template <int NW, int TPW, int XC>
+__global__ __launch_bounds__(64 * NW) void route_scores_kernel(
+    int64_t T, int H, int E, int es, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ wr, const float* __restrict__ bias, float* __restrict__ scores) {
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * TPW;
+    const int e0 = blockIdx.y * es;
+    const int e1 = e0 + es < E ? e0 + es : E;
+    u32x4 xr[TPW][XC];
+    load_token_chunks<TPW, XC>(xr, x, T, H, tok0, lane);
+    small_scores<NW, TPW, XC>(xr, wr, bias, H, e0, e1, lane, wave, [&](int t, int e, float v) {
+        if (tok0 + t < T) scores[(tok0 + t) * E + e] = v;
+    });
+}
+
+// select_topk over TT tokens' rows of scores [T, E]; one wave per token.
+template <int TT>
+__global__ __launch_bounds__(64 * TT) void route_select_kernel(
+    int64_t T, int E, int G, int TG, int k, const float* __restrict__ scores,
+    int32_t* __restrict__ ids, float* __restrict__ weights) {
+    __shared__ float s_score[TT][kMaxE + 4];
+    __shared__ float s_gscore[TT][kMaxE];
+    __shared__ unsigned char s_kept[TT][kMaxE];
+    const int64_t tok0 = static_cast<int64_t>(blockIdx.x) * TT;
+    for (int i = threadIdx.x; i < TT * E; i += 64 * TT) {
+        const int tt = i / E, e = i - tt * E;
+        int64_t t = tok0 + tt;
+        if (t > T - 1) t = T - 1;  // rows past the batch: dropped by select_topk
+        s_score[tt][e] = scores[t * E + e];
+    }
+    __syncthreads();
+    select_topk<TT, 64 * TT>(s_score, s_gscore, s_kept, tok0, TT, T, E, G, TG, k, ids, weights);
+}
+
+template <int XC>
+void launch_route_split(const Problem& p, const uint16_t* x, const uint16_t* w_router,
+                        const float* bias, int32_t* ids, float* weights, float* scores,
+                        hipStream_t s) {
+    constexpr int kSlice = 32, kSelTok = 4, kTpw = 4;
+    const dim3 grid(static_cast<unsigned>((p.T + kTpw - 1) / kTpw),
+                    static_cast<unsigned>((p.E + kSlice - 1) / kSlice));
+    route_scores_kernel<8, kTpw, XC><<<grid, dim3(512), 0, s>>>(p.T, p.H, p.E, kSlice, x, w_router,
+                                                                bias, scores);
+    const int64_t g2 = (p.T + kSelTok - 1) / kSelTok;
+    route_select_kernel<kSelTok><<<dim3(static_cast<unsigned>(g2)), dim3(64 * kSelTok), 0, s>>>(
+        p.T, p.E, p.G, p.TG, p.k, scores, ids, weights);
 }
 
 template <int TPW, int XC>
@@ -405,6 +473,23 @@ hipError_t launch_route(const Problem& p, const uint16_t* x, const uint16_t* w_r
         route_kernel<1, 16, 4><<<dim3(static_cast<unsigned>(grid)), dim3(1024), 0, s>>>(
             p.T, p.H, p.E, p.G, p.TG, p.k, tpw, x, w_router, bias, ids, weights);
     }
+    return hipGetLastError();
+}
+
+
+hipError_t launch_route_scratch(const Problem& p, const uint16_t* x, const uint16_t* w_router,
+                                const float* bias, int32_t* ids, float* weights, void* scratch,
+                                size_t scratch_bytes, hipStream_t s) {
+    const int xc = (p.H / 8 + 63) / 64;
+    const size_t need = static_cast<size_t>(p.T) * static_cast<size_t>(p.E) * 4;
+    if (p.T > 512 || xc > 16 || scratch == nullptr || scratch_bytes < need)
+        return launch_route(p, x, w_router, bias, ids, weights, s);
+    float* scores = static_cast<float*>(scratch);
+    if (xc <= 1) launch_route_split<1>(p, x, w_router, bias, ids, weights, scores, s);
+    else if (xc <= 2) launch_route_split<2>(p, x, w_router, bias, ids, weights, scores, s);
+    else if (xc <= 4) launch_route_split<4>(p, x, w_router, bias, ids, weights, scores, s);
+    else if (xc <= 10) launch_route_split<10>(p, x, w_router, bias, ids, weights, scores, s);
+    else launch_route_split<16>(p, x, w_router, bias, ids, weights, scores, s);
     return hipGetLastError();
 }
 

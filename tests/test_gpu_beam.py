@@ -70,6 +70,15 @@ def test_beam_config(moe, name, route_sample, ffn_sample):
     o_ids, o_w, s, gs = oracle.route(xs, wrb, bias, cfg.G, cfg.TG, cfg.k, want_scores=True)
     exempt, st = compare_routing(ids[rt], wts[rt], o_ids, o_w, s, gs, cfg.E, cfg.G, cfg.TG, cfg.k)
     print(f"    routed {len(rt)} tokens, exempt {st['exempt']}", flush=True)
+    if cfg.T <= 512:
+        # the forward routes small batches with the experts split over
+        # workgroups (scores through the workspace); moe_route keeps them in
+        # one workgroup: the same ids and weights, bit for bit
+        ids2 = torch.empty_like(b["topk_ids"])
+        wts2 = torch.empty_like(b["topk_weights"])
+        moe.moe_route(p, g["x"], g["w_router"], g["bias"], ids2, wts2)
+        torch.cuda.synchronize()
+        assert torch.equal(ids2, b["topk_ids"]) and torch.equal(wts2, b["topk_weights"])
     # ---- permutation of all pairs, bit-exact against the oracle's sort ----
     ws = b["ws"]
     off, sp, pr = oracle.permute(ids, cfg.E)

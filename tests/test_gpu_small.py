@@ -159,6 +159,7 @@ def test_forward_matches_steps_bf16_and_determinism(moe):
         torch.cuda.synchronize()
         outs.append(b["out"].cpu())
         np.testing.assert_array_equal(b["topk_ids"].cpu().numpy(), r["topk_ids"])
+        np.testing.assert_array_equal(b["topk_weights"].cpu().numpy(), r["topk_weights"])
     # the composed call equals the four steps, bit for bit, and repeats exactly
     np.testing.assert_array_equal(outs[0].numpy(), r["out"])
     assert torch.equal(outs[0], outs[1])
