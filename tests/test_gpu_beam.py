@@ -48,17 +48,17 @@ def _run(moe, cfg, g):
     return p, b
 
 
-@pytest.mark.parametrize("name,route_sample,ffn_sample",
-                         [("decode", None, 16), ("prefill", None, 12), ("skew", None, 12),
-                          ("long", 4096, 8)])
-def test_beam_config(moe, name, route_sample, ffn_sample):
+@pytest.mark.parametrize("name,route_sample,ffn_sample,seed",
+                         [("decode", None, 16, 0), ("decode", None, 16, 1), ("decode", None, 16, 2),
+                          ("prefill", None, 12, 0), ("skew", None, 12, 0), ("long", 4096, 8, 0)])
+def test_beam_config(moe, name, route_sample, ffn_sample, seed):
     cfg = CONFIGS[name]
-    print(f"[case] beam {name} T={cfg.T}", flush=True)
-    g = _inputs(cfg)
+    print(f"[case] beam {name} T={cfg.T} token seed {seed}", flush=True)
+    g = _inputs(cfg, seed)
     p, b = _run(moe, cfg, g)
     ids = b["topk_ids"].cpu().numpy()
     wts = b["topk_weights"].cpu().numpy()
-    rng = np.random.default_rng(cfg.T)
+    rng = np.random.default_rng(cfg.T + seed)
     # ---- routing: all tokens, or a seeded sample ----
     if route_sample is None:
         rt = np.arange(cfg.T)
