@@ -101,6 +101,10 @@ SHAPES = [
     (1500, 256, 384, 16, 4, 2, 4),      # ~375 rows per expert, I not a power of two
     (2600, 256, 128, 8, 2, 1, 2),       # ~650 rows per expert: 256 + 256 + ragged last row tile
     (2400, 256, 128, 12, 4, 2, 2),      # ~400 rows per expert, 8 does not divide E
+    (1200, 256, 128, 256, 8, 4, 16),    # the largest k, MFMA router (more than 512 tokens)
+    (200, 256, 128, 256, 8, 8, 16),     # the largest k, every group kept, small-batch router
+    (300, 256, 128, 24, 3, 2, 6),       # three groups of eight
+    (100, 256, 128, 4, 2, 1, 2),        # fewer experts than router waves
 ]
 
 
