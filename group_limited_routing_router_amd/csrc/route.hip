@@ -25,6 +25,8 @@
 // route_small_kernel (up to 512 tokens): one workgroup per token or two,
 // logits as per-lane bf16 dot products over register-held token chunks and
 // a butterfly sum over the wave (see the kernel); the same selection.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -111,15 +113,38 @@ __device__ __forceinline__ void select_topk(float (*s_score)[kMaxE + 4], float (
                     bv = v[i];
                     be = lane + 64 * i;
                 }
+            // wave arg-max under (score desc, index asc), a total order, so
+            // any reduction tree gives the same pick: DPP within each row of
+            // 16 lanes (swap neighbours, swap pairs, mirror halves, mirror
+            // the row: every lane of a row ends with the row's best), then
+            // the four rows combined from one lane each
+            auto take = [&](float ov, int oe) {  // branch-free (selects)
+                const bool t = (ov > bv) | ((ov == bv) & (oe < be));
+                bv = t ? ov : bv;
+                be = t ? oe : be;
+            };
+            auto dpp_step = [&](auto ctrl_c) {
+                constexpr int CTRL = decltype(ctrl_c)::value;
+                const int ovb = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, bv), CTRL, 0xF, 0xF, false);
+                const int oe = __builtin_amdgcn_update_dpp(0, be, CTRL, 0xF, 0xF, false);
+                take(__builtin_bit_cast(float, ovb), oe);
+            };
+            dpp_step(std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+            dpp_step(std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+            dpp_step(std::integral_constant<int, 0x141>{});  // row_half_mirror
+            dpp_step(std::integral_constant<int, 0x140>{});  // row_mirror
+            float sv = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 0));
+            int se = __builtin_amdgcn_readlane(be, 0);
 #pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) {
-                const float ov = __shfl_xor(bv, off);
-                const int oe = __shfl_xor(be, off);
-                if (ov > bv || (ov == bv && oe < be)) {
-                    bv = ov;
-                    be = oe;
-                }
+            for (int r = 1; r < 4; ++r) {
+                const float ov = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, bv), 16 * r));
+                const int oe = __builtin_amdgcn_readlane(be, 16 * r);
+                const bool t = (ov > sv) | ((ov == sv) & (oe < se));
+                sv = t ? ov : sv;
+                se = t ? oe : se;
             }
+            bv = sv;
+            be = se;
             pick_v[j] = bv;
             pick_e[j] = be;
 #pragma unroll
