@@ -212,7 +212,10 @@ moe_status moe_forward_fp8(const moe_problem* p, const moe_bf16* x, const moe_bf
 /* The whole block: route, permute, expert FFN, combine.
  *   topk_ids, topk_weights  optional [T,k] outputs (NULL: kept in `ws`)
  *   y                       [T*k,H] fp32 caller buffer for expert outputs
- *   out                     [T,H] in out_dtype */
+ *   out                     [T,H] in out_dtype
+ * Routing gives the same ids and weights, bit for bit, as moe_route; for up
+ * to 512 tokens the scores pass through the part of `ws` that later holds
+ * the SwiGLU product. */
 moe_status moe_forward(const moe_problem* p, const moe_bf16* x, const moe_bf16* w_router,
                        const float* bias, const moe_bf16* w_gate, const moe_bf16* w_up,
                        const moe_bf16* w_down, void* out, moe_dtype out_dtype, int32_t* topk_ids,
