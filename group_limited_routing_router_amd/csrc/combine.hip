@@ -8,14 +8,25 @@
 // there are no atomics and the result is deterministic.  HBM-bound: it reads
 // T*k*H fp32 and writes T*H outputs; loads are 16 B per lane and the k row
 // loads of one column chunk are independent, so k loads are in flight per
-// lane.
+// lane.  A token's workgroup takes the fewest passes over the row's float4
+// chunks that at most 1024 threads allow, with the fewest whole waves for
+// that many passes (two passes of 640 threads for a 5120-wide row: 3% faster
+// than five passes of 256 at 8192 tokens, 20% at 128).
 #include "common.h"
 #include "kernels.h"
 
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 256;         // combine + residual
+constexpr int kCombineMaxThreads = 1024;
+
+int combine_threads(int H) {
+    const int nv = H / 4;
+    const int passes = (nv + kCombineMaxThreads - 1) / kCombineMaxThreads;
+    const int per = (nv + passes - 1) / passes;
+    return (per + 63) / 64 * 64;
+}
 
 // y larger than kStreamBytes streams past the caches (nontemporal loads and
 // output stores): at prefill it is far larger than L2 plus the Infinity Cache
@@ -31,7 +42,7 @@ __device__ __forceinline__ float4 load4(const float* p, bool nt) {
 }
 
 template <int K, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int H, float scale,
+__global__ __launch_bounds__(kCombineMaxThreads) void combine_kernel(int64_t T, int H, float scale,
                                                            const float* __restrict__ y,
                                                            const int32_t* __restrict__ pair_rows,
                                                            const float* __restrict__ weights,
@@ -45,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int H, flo
         w[j] = weights[t * K + j];
     }
     const int nv = H >> 2;  // float4 chunks per row
-    for (int c = threadIdx.x; c < nv; c += kThreads) {
+    for (int c = threadIdx.x; c < nv; c += blockDim.x) {
         float4 v[K];
 #pragma unroll
         for (int j = 0; j < K; ++j) {
@@ -86,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(int64_t T, int H, flo
 template <int K>
 hipError_t launch_k(const Problem& p, const float* y, const int32_t* pair_rows,
                     const float* weights, void* out, bool out_bf16, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>(p.T)), block(kThreads);
+    const dim3 grid(static_cast<unsigned>(p.T)), block(combine_threads(p.H));
     const bool nt = p.T * p.k * static_cast<int64_t>(p.H) * 4 > kStreamBytes;
     if (out_bf16)
         combine_kernel<K, true><<<grid, block, 0, s>>>(p.T, p.H, p.scale, y, pair_rows, weights, out, nt);
