@@ -105,6 +105,8 @@ SHAPES = [
     (200, 256, 128, 256, 8, 8, 16),     # the largest k, every group kept, small-batch router
     (300, 256, 128, 24, 3, 2, 6),       # three groups of eight
     (100, 256, 128, 4, 2, 1, 2),        # fewer experts than router waves
+    (8230, 128, 64, 16, 4, 2, 4),       # above 8192 tokens: 64-token router tiles, ragged last tile
+    (8300, 256, 64, 256, 8, 4, 8),      # the same with 256 experts
 ]
 
 
