@@ -162,3 +162,20 @@ def test_binding_raises_with_message(lib):
     with pytest.raises(lib.MoEError) as ei:
         lib.moe_route(p, 0, 0, None, 0, 0, stream=0)
     assert "G=3" in str(ei.value)
+
+
+def test_header_serves_a_plain_c_program(tmp_path, lib):
+    """include/moe.h compiles as C11 with every gcc warning an error, and a C
+    program links against libmoe.so and the HIP runtime's C API.  Run with no
+    arguments it prints its usage before any HIP call."""
+    import subprocess
+    import sys
+
+    sys.path.insert(0, ROOT)
+    import __graft_entry__
+
+    lib.load_library()  # libmoe.so is built
+    exe = __graft_entry__.build_c_client(out=str(tmp_path / "moe_client"), werror=True)
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 2 and "usage" in r.stderr
+
