@@ -18,8 +18,9 @@
 namespace moe {
 namespace {
 
-constexpr int kThreads = 256;         // combine + residual
+constexpr int kThreads = 256;            // combine + residual with many tokens
 constexpr int kCombineMaxThreads = 1024;
+constexpr int64_t kWideBelowTokens = 256;  // about one workgroup per compute unit
 
 int combine_threads(int H) {
     const int nv = H / 4;
@@ -114,14 +115,16 @@ hipError_t launch_k(const Problem& p, const float* y, const int32_t* pair_rows,
 // stays in registers (NC float4 chunks per thread) between the sum of squares
 // and the update, so it never goes to memory.  The sum of squares is reduced
 // in a fixed order: per thread over its chunks, a shuffle tree in each wave,
-// then the waves in index order.
+// then the waves in index order.  The workgroup is a whole number of waves
+// (blockDim.x), each thread holding at most NC chunks.
 template <int K, int NC>
-__global__ __launch_bounds__(kThreads) void combine_residual_kernel(
+__global__ __launch_bounds__(kCombineMaxThreads) void combine_residual_kernel(
     int64_t T, int H, float scale, const float* __restrict__ y,
     const int32_t* __restrict__ pair_rows, const float* __restrict__ weights,
     const float* __restrict__ gain, float eps, float wa, float wb, float* __restrict__ res,
     bool nt) {
-    __shared__ float s_part[kThreads / 64];
+    __shared__ float s_part[kCombineMaxThreads / 64];
+    const int nth = blockDim.x;
     const int64_t t = blockIdx.x;
     int32_t row[K];
     float w[K];
@@ -135,7 +138,7 @@ __global__ __launch_bounds__(kThreads) void combine_residual_kernel(
     float ss = 0.0f;
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-        const int c = threadIdx.x + i * kThreads;
+        const int c = threadIdx.x + i * nth;
         o[i] = make_float4(0.f, 0.f, 0.f, 0.f);
         if (c < nv) {
             float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -164,14 +167,13 @@ __global__ __launch_bounds__(kThreads) void combine_residual_kernel(
     if ((threadIdx.x & 63) == 0) s_part[threadIdx.x >> 6] = ss;
     __syncthreads();
     float tot = s_part[0];
-#pragma unroll
-    for (int i = 1; i < kThreads / 64; ++i) tot = tot + s_part[i];
+    for (int i = 1; i < (nth >> 6); ++i) tot = tot + s_part[i];
     const float inv = 1.0f / sqrtf(tot / static_cast<float>(H) + eps);
     float4* r4 = reinterpret_cast<float4*>(res + t * H);
     const float4* g4 = reinterpret_cast<const float4*>(gain);
 #pragma unroll
     for (int i = 0; i < NC; ++i) {
-        const int c = threadIdx.x + i * kThreads;
+        const int c = threadIdx.x + i * nth;
         if (c < nv) {
             const float4 g = g4[c];
             float4 r = r4[c];
@@ -188,8 +190,12 @@ template <int K>
 hipError_t launch_residual_k(const Problem& p, const float* y, const int32_t* pair_rows,
                              const float* weights, const float* gain, float eps, float wa,
                              float wb, float* res, hipStream_t s) {
-    const dim3 grid(static_cast<unsigned>(p.T)), block(kThreads);
-    const int chunks = (p.H / 4 + kThreads - 1) / kThreads;
+    // fewer tokens than compute units: the combine's wide workgroups (10.3 ->
+    // 6.4 us at 128 tokens); otherwise 256 threads, whose shorter wait at the
+    // barrier wins with many tokens (640 were 8% slower at 8192)
+    const int threads = p.T < kWideBelowTokens ? combine_threads(p.H) : kThreads;
+    const dim3 grid(static_cast<unsigned>(p.T)), block(threads);
+    const int chunks = (p.H / 4 + threads - 1) / threads;
     const bool nt = p.T * p.k * static_cast<int64_t>(p.H) * 4 > kStreamBytes;
 #define MOE_RES(NC)                                                                       \
     combine_residual_kernel<K, NC><<<grid, block, 0, s>>>(p.T, p.H, p.scale, y, pair_rows, \

@@ -34,7 +34,8 @@ CASES = [
     (64, 256, 128, 16, 4, 2, 4, 1.0, 1),
     (64, 256, 128, 16, 4, 2, 4, 2.5, 2),
     (37, 512, 64, 8, 2, 1, 2, 2.5, 7),
-    (50, 2176, 64, 16, 4, 2, 4, 2.5, 3),      # 544 float4 chunks: three per thread, ragged
+    (50, 2176, 64, 16, 4, 2, 4, 2.5, 3),      # 544 float4 chunks: one pass of 9 waves
+    (300, 2176, 64, 16, 4, 2, 4, 2.5, 9),     # the same row with 256 threads: three chunks each, ragged
     (40, 5120, 128, 16, 4, 2, 4, 2.5, 104),   # Beam width
     (16, 16384, 64, 8, 2, 1, 2, 2.5, 5),      # the widest row the fused call takes
     (2048, 5120, 64, 16, 4, 2, 8, 2.5, 3),    # y of 335 MB: read past the caches (nontemporal)
