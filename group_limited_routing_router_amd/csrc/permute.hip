@@ -12,6 +12,8 @@
 //               place inside its expert is found with wave ballots (match on
 //               the expert id bits) plus the counts of the waves before it, so
 //               the order is the pair order and no atomics touch the outputs.
+// Up to kPermuteChunk pairs (decode batches) one workgroup does all three
+// steps in LDS in a single launch, with the same scatter.
 #include "common.h"
 #include "kernels.h"
 
@@ -37,53 +39,28 @@ __global__ __launch_bounds__(kThreads) void permute_count_kernel(
         counts[static_cast<int64_t>(blockIdx.x) * E + e] = hist[e];
 }
 
-// counts[b][e] becomes the first sorted position of block b's pairs of
-// expert e; offsets[e] the first position of expert e.
-__global__ __launch_bounds__(kThreads) void permute_scan_kernel(int nblocks, int E,
-                                                                int32_t* __restrict__ counts,
-                                                                int32_t* __restrict__ offsets) {
-    __shared__ int32_t tot[kThreads];
-    const int e = threadIdx.x;
-    int32_t run = 0;
-    if (e < E) {
-        for (int b = 0; b < nblocks; ++b) {
-            const int32_t c = counts[static_cast<int64_t>(b) * E + e];
-            counts[static_cast<int64_t>(b) * E + e] = run;
-            run += c;
-        }
-    }
-    tot[e] = (e < E) ? run : 0;
-    __syncthreads();
-    // inclusive Hillis-Steele scan of the per-expert totals
+// Exclusive prefix sum over tot[0..kThreads) in LDS (inclusive Hillis-Steele
+// scan, left in tot); thread e gets the sum of tot[0..e).  Every thread of
+// the workgroup calls it, after tot is written and the workgroup synchronised.
+__device__ __forceinline__ int32_t exclusive_scan(int32_t* tot, int e) {
     for (int d = 1; d < kThreads; d <<= 1) {
         const int32_t v = (e >= d) ? tot[e - d] : 0;
         __syncthreads();
         tot[e] += v;
         __syncthreads();
     }
-    const int32_t start = (e == 0) ? 0 : tot[e - 1];
-    if (e < E) {
-        offsets[e] = start;
-        for (int b = 0; b < nblocks; ++b) counts[static_cast<int64_t>(b) * E + e] += start;
-    }
-    if (e == E - 1) offsets[E] = tot[e];
+    return (e == 0) ? 0 : tot[e - 1];
 }
 
-__global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
-    int64_t pairs, int E, const int32_t* __restrict__ ids, const int32_t* __restrict__ counts,
-    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_rows) {
-    __shared__ int32_t base[kMaxE];
-    __shared__ int32_t wcount[kThreads / kWave][kMaxE];
+// Places the pairs [p0, p1) in pair order: base[e] holds the first free
+// sorted position of expert e and is advanced past each 256-pair step;
+// wcount must start at zero (it is zero again on return).  Every thread of
+// the workgroup calls it.
+__device__ void scatter_pairs(int64_t p0, int64_t p1, int E, const int32_t* __restrict__ ids,
+                              int32_t* base, int32_t (*wcount)[kMaxE],
+                              int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_rows) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    for (int e = tid; e < E; e += kThreads) {
-        base[e] = counts[static_cast<int64_t>(blockIdx.x) * E + e];
-#pragma unroll
-        for (int w = 0; w < kThreads / kWave; ++w) wcount[w][e] = 0;
-    }
-    __syncthreads();
     const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kPermuteChunk;
-    const int64_t p1 = p0 + kPermuteChunk < pairs ? p0 + kPermuteChunk : pairs;
     for (int64_t s = p0; s < p1; s += kThreads) {
         const int64_t p = s + tid;
         int e = (p < p1) ? ids[p] : -1;
@@ -119,6 +96,80 @@ __global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
     }
 }
 
+// counts[b][e] becomes the first sorted position of block b's pairs of
+// expert e; offsets[e] the first position of expert e.
+__global__ __launch_bounds__(kThreads) void permute_scan_kernel(int nblocks, int E,
+                                                                int32_t* __restrict__ counts,
+                                                                int32_t* __restrict__ offsets) {
+    __shared__ int32_t tot[kThreads];
+    const int e = threadIdx.x;
+    int32_t run = 0;
+    if (e < E) {
+        for (int b = 0; b < nblocks; ++b) {
+            const int32_t c = counts[static_cast<int64_t>(b) * E + e];
+            counts[static_cast<int64_t>(b) * E + e] = run;
+            run += c;
+        }
+    }
+    tot[e] = (e < E) ? run : 0;
+    __syncthreads();
+    const int32_t start = exclusive_scan(tot, e);
+    if (e < E) {
+        offsets[e] = start;
+        for (int b = 0; b < nblocks; ++b) counts[static_cast<int64_t>(b) * E + e] += start;
+    }
+    if (e == E - 1) offsets[E] = tot[e];
+}
+
+__global__ __launch_bounds__(kThreads) void permute_scatter_kernel(
+    int64_t pairs, int E, const int32_t* __restrict__ ids, const int32_t* __restrict__ counts,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_rows) {
+    __shared__ int32_t base[kMaxE];
+    __shared__ int32_t wcount[kThreads / kWave][kMaxE];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kThreads) {
+        base[e] = counts[static_cast<int64_t>(blockIdx.x) * E + e];
+#pragma unroll
+        for (int w = 0; w < kThreads / kWave; ++w) wcount[w][e] = 0;
+    }
+    __syncthreads();
+    const int64_t p0 = static_cast<int64_t>(blockIdx.x) * kPermuteChunk;
+    const int64_t p1 = p0 + kPermuteChunk < pairs ? p0 + kPermuteChunk : pairs;
+    scatter_pairs(p0, p1, E, ids, base, wcount, sorted_pairs, pair_rows);
+}
+
+// All three steps for at most kPermuteChunk pairs in one workgroup: the
+// histogram, its scan into expert_offsets and the scatter, all in LDS.
+__global__ __launch_bounds__(kThreads) void permute_single_kernel(
+    int64_t pairs, int E, const int32_t* __restrict__ ids, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pairs, int32_t* __restrict__ pair_rows) {
+    __shared__ int32_t base[kMaxE];
+    __shared__ int32_t tot[kThreads];
+    __shared__ int32_t wcount[kThreads / kWave][kMaxE];
+    const int tid = threadIdx.x;
+    for (int e = tid; e < E; e += kThreads) {
+        base[e] = 0;
+#pragma unroll
+        for (int w = 0; w < kThreads / kWave; ++w) wcount[w][e] = 0;
+    }
+    __syncthreads();
+    for (int64_t p = tid; p < pairs; p += kThreads) {
+        const int e = ids[p];
+        if (e >= 0 && e < E) atomicAdd(&base[e], 1);  // LDS counter; the count is exact
+    }
+    __syncthreads();
+    tot[tid] = (tid < E) ? base[tid] : 0;
+    __syncthreads();
+    const int32_t start = exclusive_scan(tot, tid);
+    if (tid < E) {
+        offsets[tid] = start;
+        base[tid] = start;
+    }
+    if (tid == E - 1) offsets[E] = tot[tid];
+    __syncthreads();
+    scatter_pairs(0, pairs, E, ids, base, wcount, sorted_pairs, pair_rows);
+}
+
 }  // namespace
 
 hipError_t launch_permute(const Problem& p, const int32_t* ids, int32_t* offsets,
@@ -126,6 +177,11 @@ hipError_t launch_permute(const Problem& p, const int32_t* ids, int32_t* offsets
                           hipStream_t s) {
     const int64_t pairs = p.T * p.k;
     const int64_t nb = permute_blocks(pairs);
+    if (nb == 1) {
+        permute_single_kernel<<<dim3(1), dim3(kThreads), 0, s>>>(pairs, p.E, ids, offsets,
+                                                                 sorted_pairs, pair_rows);
+        return hipGetLastError();
+    }
     permute_count_kernel<<<dim3(static_cast<unsigned>(nb)), dim3(kThreads), 0, s>>>(pairs, p.E, ids,
                                                                                 block_counts);
     permute_scan_kernel<<<dim3(1), dim3(kThreads), 0, s>>>(static_cast<int>(nb), p.E, block_counts,
