@@ -86,7 +86,8 @@ struct FfnArgs {
 // every row tile but the last the same multiple of GRAN rows (for the large
 // tile, whose two row waves take alternate 32-row blocks: 64-row multiples
 // keep them equally busy).  Returns false for surplus workgroups (uniform
-// over the workgroup).
+// over the workgroup).  s_off holds kMaxE + 1 entries, s_tstart
+// kMaxE + 1 + kWaves.
 template <int BM, int GRAN = 1>
 __device__ bool find_tile(const FfnArgs& a, int ncol_tiles, int32_t* s_off, int32_t* s_tstart,
                           int& e_out, int& nt_out, int& row0_out, int& rows_out) {
@@ -107,16 +108,19 @@ __device__ bool find_tile(const FfnArgs& a, int ncol_tiles, int32_t* s_off, int3
         const int n = s_off[ex + 1] - s_off[ex];
         cnt = n > 0 ? (n + BM - 1) / BM : 0;
     }
-    s_tstart[tid] = cnt;  // kThreads == kMaxE
-    __syncthreads();
-    for (int d = 1; d < kThreads; d <<= 1) {
-        const int v = tid >= d ? s_tstart[tid - d] : 0;
-        __syncthreads();
-        s_tstart[tid] += v;
-        __syncthreads();
+    // inclusive prefix sum over positions (kThreads == kMaxE): within each
+    // wave by shuffles, then the totals of the waves before it
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    int incl = cnt;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        const int v = __shfl_up(incl, d, kWave);
+        if (lane >= d) incl += v;
     }
-    const int incl = s_tstart[tid];
+    int32_t* s_wave_total = s_tstart + (kMaxE + 1);
+    if (lane == kWave - 1) s_wave_total[wave] = incl;
     __syncthreads();
+    for (int w = 0; w < wave; ++w) incl += s_wave_total[w];
     s_tstart[tid + 1] = incl;  // exclusive prefix over positions; s_tstart[E] = total row tiles
     if (tid == 0) s_tstart[0] = 0;
     __syncthreads();
@@ -197,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t s_a[2][BM * A_STRIDE];
     __shared__ __attribute__((aligned(16))) unsigned char s_b[2][BN * B_STRIDE];
     __shared__ int32_t s_off[kMaxE + 1];
-    __shared__ int32_t s_tstart[kMaxE + 1];
+    __shared__ int32_t s_tstart[kMaxE + 1 + kWaves];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
