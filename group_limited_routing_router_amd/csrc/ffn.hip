@@ -778,6 +778,22 @@ hipError_t launch_gemm_dma(const FfnArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// Tile height from the mean rows per expert (the host does not read the
+// counts back).  16-row tiles while nearly every expert fits in one: a mean
+// of at most 12 (at 128 tokens the mean is 4 and the busiest expert about
+// 12).  Above that the large tile, which streams the weights as fast with few
+// rows and takes up to 256 rows in one row tile.  Between the two, 16- or
+// 64-row tiles split the busier experts into several row tiles, each of which
+// streams that expert's weights again (3072 tokens: 5.8 ms per layer with
+// 64-row tiles, 3.9 ms with the large tile).  The 64-row tile remains for
+// shapes the large tile does not take.
+constexpr int64_t kSmallTileMaxRows = 12;
+// With FP8 weights the large tile streams more slowly at few rows (it widens
+// the codes inside its MFMA loop): 64-row tiles up to a mean of 48 rows
+// (1536 tokens: 2.29 ms for the expert FFN against 2.44 ms), the large tile
+// above (2048 tokens: 2.68 against 2.88 ms).
+constexpr int64_t kFp8MidTileMaxRows = 48;
+
 hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* sorted_pairs,
                           const int32_t* offsets, const uint16_t* w_gate, const uint16_t* w_up,
                           uint16_t* h, hipStream_t s) {
@@ -787,11 +803,11 @@ hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* so
     const int64_t rows_per_expert = P / p.E;
     // weight streaming in stages of K = 128 (H % 128 == 0 holds for every
     // accepted problem)
-    if (rows_per_expert <= 24) return launch_gemm<16, 128, 1, 4, true, false, 128>(a, s);
+    if (rows_per_expert <= kSmallTileMaxRows)
+        return launch_gemm<16, 128, 1, 4, true, false, 128>(a, s);
     // the large-tile kernel addresses x with 32-bit buffer offsets
     const bool x_fits = p.T * static_cast<int64_t>(p.H) * 2 < (static_cast<int64_t>(1) << 31);
-    if (rows_per_expert <= 96 || p.I % 128 != 0 || !x_fits)
-        return launch_gemm<64, 128, 1, 4, true>(a, s);
+    if (p.I % 128 != 0 || !x_fits) return launch_gemm<64, 128, 1, 4, true>(a, s);
     return launch_gemm_dma<true>(a, s);
 }
 
@@ -802,13 +818,12 @@ hipError_t launch_down(const Problem& p, const uint16_t* h, const int32_t* offse
               nullptr};
     a.stream_out = P * static_cast<int64_t>(p.H) * 4 > kStreamBytes;
     const int64_t rows_per_expert = P / p.E;
-    if (rows_per_expert <= 24) {
+    if (rows_per_expert <= kSmallTileMaxRows) {
         // stages of K = 128 where I allows
         if (p.I % 128 == 0) return launch_gemm<16, 64, 1, 4, false, false, 128>(a, s);
         return launch_gemm<16, 64, 1, 4, false>(a, s);
     }
-    if (rows_per_expert <= 96 || p.H % 256 != 0 || p.I % 128 != 0)
-        return launch_gemm<64, 128, 1, 4, false>(a, s);
+    if (p.H % 256 != 0 || p.I % 128 != 0) return launch_gemm<64, 128, 1, 4, false>(a, s);
     return launch_gemm_dma<false>(a, s);
 }
 
@@ -835,9 +850,9 @@ hipError_t launch_expert_ffn_fp8(const Problem& p, const uint16_t* x, const int3
     // and H % 128 == 0 holds for every accepted problem; down: where I allows)
     const bool x_fits = p.T * static_cast<int64_t>(p.H) * 2 < (static_cast<int64_t>(1) << 31);
     hipError_t err;
-    if (rows_per_expert <= 24)
+    if (rows_per_expert <= kSmallTileMaxRows)
         err = launch_gemm<16, 128, 1, 4, true, true, 128>(gu, s);
-    else if (rows_per_expert <= 96 || p.I % 128 != 0 || !x_fits)
+    else if (rows_per_expert <= kFp8MidTileMaxRows || p.I % 128 != 0 || !x_fits)
         err = launch_gemm<64, 128, 1, 4, true, true, 128>(gu, s);
     else
         err = launch_gemm_dma<true, true>(gu, s);
@@ -845,8 +860,9 @@ hipError_t launch_expert_ffn_fp8(const Problem& p, const uint16_t* x, const int3
     FfnArgs dn{P, p.T, p.k, p.E, p.I, p.H, h, nullptr, offsets, w_down, nullptr, y, s_down,
                nullptr};
     dn.stream_out = P * static_cast<int64_t>(p.H) * 4 > kStreamBytes;
-    if (rows_per_expert <= 24 && p.I % 128 == 0) return launch_gemm<16, 64, 1, 4, false, true, 128>(dn, s);
-    if (rows_per_expert <= 96 || p.H % 256 != 0 || p.I % 128 != 0) {
+    if (rows_per_expert <= kSmallTileMaxRows && p.I % 128 == 0)
+        return launch_gemm<16, 64, 1, 4, false, true, 128>(dn, s);
+    if (rows_per_expert <= kFp8MidTileMaxRows || p.H % 256 != 0 || p.I % 128 != 0) {
         if (p.I % 128 == 0) return launch_gemm<64, 128, 1, 4, false, true, 128>(dn, s);
         return launch_gemm<64, 128, 1, 4, false, true>(dn, s);
     }

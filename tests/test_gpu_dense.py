@@ -26,8 +26,9 @@ def moe():
 
 CASES = [
     # (T, H, I, sampled tokens or 0 for all)
-    (20, 256, 128, 0),        # 16-row tiles
-    (64, 512, 256, 0),        # 64-row tiles
+    (12, 256, 128, 0),        # 16-row tiles
+    (64, 512, 256, 0),        # large tiles, one partly filled row tile
+    (64, 384, 192, 0),        # I and H off the large tile's multiples: 64-row tiles
     (300, 512, 384, 0),       # large tiles with a ragged second row tile
     (1000, 256, 1024, 0),
     (2048, 5120, 2048, 24),   # Beam width, large tiles, sampled

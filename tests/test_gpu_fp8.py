@@ -45,11 +45,13 @@ def _run(moe, cfg, d, w):
 
 SMALL = [
     # (T, H, I, E, G, TG, k)
-    (64, 256, 128, 16, 4, 2, 4),      # ~16 rows per expert: 16-row tiles
+    (40, 256, 128, 16, 4, 2, 4),      # ~10 rows per expert: 16-row tiles
+    (64, 256, 128, 16, 4, 2, 4),      # ~16 rows per expert: 64-row tiles
     (600, 512, 256, 16, 4, 2, 4),     # ~150 rows per expert: large tiles, ragged tails
     (33, 384, 192, 32, 4, 2, 6),
-    (300, 256, 192, 8, 2, 1, 2),      # ~75 rows per expert: 64-row tiles
-    (300, 256, 256, 8, 2, 1, 2),      # 64-row tiles, both reductions in stages of 128
+    (300, 256, 192, 8, 2, 1, 2),      # ~75 rows per expert, I not a multiple of 128: 64-row tiles
+    (160, 256, 256, 8, 2, 1, 2),      # ~40 rows per expert: 64-row tiles, both reductions in stages of 128
+    (300, 256, 256, 8, 2, 1, 2),      # ~75 rows per expert: large tiles
 ]
 
 

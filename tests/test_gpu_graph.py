@@ -21,7 +21,7 @@ def moe():
 
 CASES = [
     # (T, H, I, E, G, TG, k): 16-row tiles; large tiles with ragged tails
-    (64, 256, 128, 16, 4, 2, 4),
+    (40, 256, 128, 16, 4, 2, 4),
     (600, 512, 256, 16, 4, 2, 4),
 ]
 
