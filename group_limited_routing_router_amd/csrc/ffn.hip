@@ -368,6 +368,13 @@ hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+// The large tile reads its operands through buffer resources with 32-bit
+// offsets.  A stage row past the tile's last 32-row block gets this offset,
+// which lies past the end of any operand the kernel takes (x of at most
+// kNoRowOffset bytes, so up to 4 GiB less 1 MiB) and cannot wrap when a
+// stage's K offset is added, so its loads fetch nothing.
+constexpr uint32_t kNoRowOffset = 0xFFF00000u;
+
 // Large-tile GEMM for experts with many rows (prefill and longer).
 //
 // 32x32x16 MFMA; a 256-thread workgroup owns a 256 x 256 tile and each of its
@@ -459,7 +466,6 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
     // ---- DMA addressing: wave w fills rows [64 w, 64 w + 64) of a stage,
     // 8 rows per load; lane L of load j writes row 64 w + 8 j + L / 8, physical
     // chunk L % 8, i.e. logical chunk (L % 8) ^ ((row >> 1) & 7). ----
-    constexpr uint32_t kOutside = 0x80000000u;
     __amdgpu_buffer_rsrc_t rsrc_a, rsrc_b;
     uint32_t va[DMA_A], vb[DMA_BS];
     if constexpr (GATEUP)
@@ -482,7 +488,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
         const int c = (lane & 7) ^ ((r >> 1) & 7);
         uint32_t av;
         if (r >= nblk * 32) {
-            av = kOutside;
+            av = kNoRowOffset;
         } else if constexpr (GATEUP) {
             const int rr = min(r, rows - 1);
             int64_t tok = a.sorted_pairs[row0 + rr] / a.k;
@@ -806,7 +812,7 @@ hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* so
     if (rows_per_expert <= kSmallTileMaxRows)
         return launch_gemm<16, 128, 1, 4, true, false, 128>(a, s);
     // the large-tile kernel addresses x with 32-bit buffer offsets
-    const bool x_fits = p.T * static_cast<int64_t>(p.H) * 2 < (static_cast<int64_t>(1) << 31);
+    const bool x_fits = p.T * static_cast<int64_t>(p.H) * 2 <= static_cast<int64_t>(kNoRowOffset);
     if (p.I % 128 != 0 || !x_fits) return launch_gemm<64, 128, 1, 4, true>(a, s);
     return launch_gemm_dma<true>(a, s);
 }
@@ -848,7 +854,7 @@ hipError_t launch_expert_ffn_fp8(const Problem& p, const uint16_t* x, const int3
     // few rows per expert: the weight stream is the cost; stages of K = 128
     // make every weight row of a stage one whole 128-byte line (gate/up: K = H,
     // and H % 128 == 0 holds for every accepted problem; down: where I allows)
-    const bool x_fits = p.T * static_cast<int64_t>(p.H) * 2 < (static_cast<int64_t>(1) << 31);
+    const bool x_fits = p.T * static_cast<int64_t>(p.H) * 2 <= static_cast<int64_t>(kNoRowOffset);
     hipError_t err;
     if (rows_per_expert <= kSmallTileMaxRows)
         err = launch_gemm<16, 128, 1, 4, true, true, 128>(gu, s);

@@ -48,8 +48,8 @@ def _run(moe, cfg, g):
     return p, b
 
 
-# "huge": 212992 tokens, x above 2 GiB: the gate/up projection leaves the
-# large-tile kernel (32-bit buffer offsets into x) for the 64-row kernel
+# "huge": 212992 tokens, x above 2 GiB: the large tile's 32-bit buffer
+# offsets into x pass 2^31 (unsigned) for the later tokens
 @pytest.mark.parametrize("name,route_sample,ffn_sample,seed",
                          [("decode", None, 16, 0), ("decode", None, 16, 1), ("decode", None, 16, 2),
                           ("prefill", None, 12, 0), ("skew", None, 12, 0), ("long", 4096, 8, 0),
