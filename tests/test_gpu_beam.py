@@ -48,14 +48,23 @@ def _run(moe, cfg, g):
     return p, b
 
 
+# "mid": 1536 tokens, about 48 rows per expert, a serving-size batch on the
+# large tile with mostly partly filled row tiles.
 # "huge": 212992 tokens, x above 2 GiB: the large tile's 32-bit buffer
 # offsets into x pass 2^31 (unsigned) for the later tokens
+EXTRA = {"mid": ("prefill", 1536), "huge": ("long", 212992)}
+
+
 @pytest.mark.parametrize("name,route_sample,ffn_sample,seed",
                          [("decode", None, 16, 0), ("decode", None, 16, 1), ("decode", None, 16, 2),
-                          ("prefill", None, 12, 0), ("skew", None, 12, 0), ("long", 4096, 8, 0),
-                          ("huge", 1024, 8, 0)])
+                          ("mid", None, 12, 0), ("prefill", None, 12, 0), ("skew", None, 12, 0),
+                          ("long", 4096, 8, 0), ("huge", 1024, 8, 0)])
 def test_beam_config(moe, name, route_sample, ffn_sample, seed):
-    cfg = CONFIGS[name] if name != "huge" else CONFIGS["long"].with_(name="huge", T=212992)
+    if name in EXTRA:
+        base, T = EXTRA[name]
+        cfg = CONFIGS[base].with_(name=name, T=T)
+    else:
+        cfg = CONFIGS[name]
     if name == "huge":
         assert cfg.T * cfg.H * 2 >= 2 ** 31
     print(f"[case] beam {name} T={cfg.T} token seed {seed}", flush=True)
