@@ -7,22 +7,38 @@ A step is one moe_forward call (router, group-limited top-k, permutation,
 gate/up + SwiGLU GEMM, down GEMM, weighted combine) over T tokens that are
 already resident in HBM.  The default workload is the prefill chunk: T=8192
 tokens, hidden 5120, 256 experts in 8 groups (4 kept), k=8, intermediate
-2560, bf16 weights and activations with fp32 accumulation; the decode batch
-(T=128) is timed as well because its HBM-bandwidth fraction is the other half
-of the headline metric.  Inputs are seeded synthetic Gaussians (no trained
-weights exist here).
+2560, bf16 weights and activations with fp32 accumulation.  The decode batch
+(T=128, the HBM half of the headline metric), the skewed (T=4096) and long
+(T=65536) workloads are timed the same way and reported as secondary objects,
+with the FP8-weight layer and the dense MLP.  Inputs are seeded synthetic
+Gaussians (no trained weights exist here).
 
-Prints one JSON line.  `value` is tokens/s of the timed workload; `roofline`
+Prints one JSON line.  `value` is tokens/s of the timed workload (mean wall
+time of exactly --steps calls between two device synchronisations; the
+median and minimum per-step event times are reported beside it); `roofline`
 describes the dominant kernel (timed with HIP events on the stream the
-library launches on); `cpu_baseline` is the CPU oracle timed on a bounded
-sample of the same workload on this host's cores.
+library launches on); `achievable_*` are this GPU's measured streaming-read
+bandwidth and back-to-back MFMA rate (the measurement kernels of
+include/moe_peak.h); `cpu_baseline` is the CPU oracle timed on this host's
+cores (every decode token, samples of prefill and skew, long extrapolated).
+
+Other modes (one JSON line or a text table each):
+  --kernels-only       only the timed workload's separate calls (the kernel
+                       trace of such a run holds nothing else)
+  --gemm-study         the prefill expert GEMMs at fixed rows per expert
+  --summarize-trace D  per-kernel durations from a rocprofv3 kernel trace
+  --summarize-pmc D1 D2  HBM bytes per launch from FETCH_SIZE / WRITE_SIZE runs
 """
 from __future__ import annotations
 
 import argparse
+import csv
+import glob
 import hashlib
 import json
 import os
+import re
+import statistics
 import sys
 import time
 
@@ -33,10 +49,13 @@ if ROOT not in sys.path:
 PEAK_BF16 = 2.5166e15   # dense bf16 MFMA, FLOP/s (MI355X published)
 PEAK_HBM = 8.0e12       # HBM3E, B/s (MI355X published)
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+# the sources of the MoE block's kernels (the measurement kernels of peak.hip
+# are not part of the block and do not invalidate its stored traffic)
 KERNEL_SOURCES = sorted(
     os.path.join("group_limited_routing_router_amd", "csrc", f)
     for f in os.listdir(os.path.join(ROOT, "group_limited_routing_router_amd", "csrc"))
-    if f.endswith((".hip", ".h")))
+    if f.endswith((".hip", ".h")) and f != "peak.hip")
+STEPS = ["route", "permute", "gate_up", "down", "combine", "combine_residual"]
 
 
 def log(*a):
@@ -73,7 +92,36 @@ def work_counts(cfg, n_hit):
     return c, layer
 
 
-def run_workload(name, steps, warmup, weights, want_kernels=True):
+def timed_steps(step, steps, warmup):
+    """warmup untimed calls, then exactly `steps` calls bracketed by a device
+    synchronisation on both sides (wall clock), with an event on the current
+    stream between consecutive calls.  Returns (mean wall ms per step, the
+    per-step event times in ms)."""
+    import torch
+
+    for _ in range(warmup):
+        step()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev[0].record()
+    for i in range(steps):
+        step()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall * 1e3 / steps, [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
+def step_stats(step_ms):
+    """Median and minimum of the per-step event times."""
+    return {"ms_median": round(statistics.median(step_ms), 4), "ms_min": round(min(step_ms), 4)}
+
+
+def run_workload(name, steps, warmup, weights, forward=True, kernels=True):
+    """One workload on the bf16 weights: the timed forward (if `forward`) and
+    each step as a separate entry-point call bracketed by events on the
+    current stream (if `kernels`)."""
     import torch
 
     from group_limited_routing_router_amd import moe
@@ -89,26 +137,11 @@ def run_workload(name, steps, warmup, weights, want_kernels=True):
         moe.moe_forward(p, d["x"], d["w_router"], d["bias"], d["w_gate"], d["w_up"], d["w_down"],
                         b["out"], b["topk_ids"], b["topk_weights"], b["y"], b["ws"])
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms = wall * 1e3 / steps
-
-    ids = b["topk_ids"]
-    n_hit = int((torch.bincount(ids.flatten().long(), minlength=cfg.E) > 0).sum())
-    counts, layer = work_counts(cfg, n_hit)
-    res = dict(cfg=cfg, ms=ms, n_hit=n_hit, counts=counts, layer=layer, buffers=b, inputs=d)
-
-    if want_kernels:
-        # the same steps as separate calls, each bracketed by events on the
-        # current stream (the stream the library launches on)
-        names = ["route", "permute", "gate_up", "down", "combine", "combine_residual"]
-        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    res = dict(cfg=cfg, buffers=b, inputs=d)
+    if forward:
+        res["ms"], res["step_ms"] = timed_steps(step, steps, warmup)
+    if kernels:
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STEPS) + 1)]
               for _ in range(steps)]
         gain = torch.ones(cfg.H, dtype=torch.float32, device="cuda")
         stream_res = torch.zeros((cfg.T, cfg.H), dtype=torch.float32, device="cuda")
@@ -131,17 +164,46 @@ def run_workload(name, steps, warmup, weights, want_kernels=True):
                                      stream_res)
             if e: e[6].record()
         torch.cuda.synchronize()
-        kt = {}
-        for j, nm in enumerate(names):
-            kt[nm] = sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps
-        res["kernel_ms"] = kt
+        res["kernel_ms"] = {nm: sum(ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)) / steps
+                            for j, nm in enumerate(STEPS)}
+        del stream_res
+    ids = b["topk_ids"]
+    res["n_hit"] = int((torch.bincount(ids.flatten().long(), minlength=cfg.E) > 0).sum())
+    res["counts"], res["layer"] = work_counts(cfg, res["n_hit"])
+    if cfg.hot_groups:
+        hot = torch.nonzero(d["bias"] > 0).flatten()
+        res["hot_share"] = round(float(torch.isin(ids.flatten(), hot.to(ids.dtype)).float().mean()), 4)
     return res
 
 
+def workload_summary(res, peaks=None):
+    """The secondary object of a workload: times, rates, fractions of the
+    published (and, if measured, the achievable) peaks, per-step times and
+    the roofline of its dominant kernel."""
+    cfg, ms, layer = res["cfg"], res["ms"], res["layer"]
+    kms = res["kernel_ms"]
+    dominant = max((k for k in kms if k != "combine_residual"), key=kms.get)
+    out = {"tokens": cfg.T, "ms_per_step": round(ms, 4), **step_stats(res["step_ms"]),
+           "tokens_per_s": round(cfg.T / (ms * 1e-3), 1), "experts_hit": res["n_hit"],
+           "tflops": round(layer["flops"] / (ms * 1e-3) / 1e12, 1),
+           "mfma_frac": round(layer["flops"] / (ms * 1e-3) / PEAK_BF16, 4),
+           "hbm_gbs": round(layer["bytes"] / (ms * 1e-3) / 1e9, 1),
+           "hbm_frac": round(layer["bytes"] / (ms * 1e-3) / PEAK_HBM, 4)}
+    if peaks:
+        out["mfma_frac_of_achievable"] = round(
+            layer["flops"] / (ms * 1e-3) / 1e12 / peaks["achievable_mfma_tflops"], 4)
+        out["hbm_frac_of_achievable"] = round(
+            layer["bytes"] / (ms * 1e-3) / 1e9 / peaks["achievable_hbm_gbs"], 4)
+    if "hot_share" in res:
+        out["hot_expert_share"] = res["hot_share"]
+    out["kernels_ms"] = {k: round(v, 4) for k, v in kms.items() if k != "combine_residual"}
+    out["roofline"] = roofline_for(res, dominant)
+    return out
+
+
 def run_fp8(name, steps, warmup, weights_fp8):
-    """The block with FP8 expert weights (moe_forward_fp8) on a workload, timed
-    with events on the current stream; algorithmic bytes count one byte per
-    weight plus the per-channel scales."""
+    """The block with FP8 expert weights (moe_forward_fp8) on a workload;
+    algorithmic bytes count one byte per weight plus the per-channel scales."""
     import torch
 
     from group_limited_routing_router_amd import moe
@@ -158,29 +220,22 @@ def run_fp8(name, steps, warmup, weights_fp8):
                             w["q_up"], w["s_up"], w["q_down"], w["s_down"], b["out"],
                             b["topk_ids"], b["topk_weights"], b["y"], b["ws"])
 
-    for _ in range(warmup):
-        step()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms, step_ms = timed_steps(step, steps, warmup)
     n_hit = int((torch.bincount(b["topk_ids"].flatten().long(), minlength=cfg.E) > 0).sum())
     T, H, I, E, k = cfg.T, cfg.H, cfg.I, cfg.E, cfg.k
     flops = 2 * T * H * E + 6 * T * k * H * I
     bytes_ = n_hit * (3 * I * H + (2 * I + H) * 4) + E * H * 2 + T * H * 2 + T * H * 4
-    return {"tokens": T, "ms_per_step": round(ms, 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+    del b, d
+    torch.cuda.empty_cache()
+    return {"tokens": T, "ms_per_step": round(ms, 4), **step_stats(step_ms),
+            "tokens_per_s": round(T / (ms * 1e-3), 1),
             "experts_hit": n_hit, "hbm_gbs": round(bytes_ / (ms * 1e-3) / 1e9, 1),
             "hbm_frac": round(bytes_ / (ms * 1e-3) / PEAK_HBM, 4),
             "mfma_frac": round(flops / (ms * 1e-3) / PEAK_BF16, 4)}
 
 
 def run_dense(steps, warmup):
-    """The dense SwiGLU MLP (moe_dense_mlp) on its synthetic workload, timed
-    with events on the current stream."""
+    """The dense SwiGLU MLP (moe_dense_mlp) on its synthetic workload."""
     import torch
 
     from group_limited_routing_router_amd import moe
@@ -195,26 +250,73 @@ def run_dense(steps, warmup):
     def step():
         moe.moe_dense_mlp(p, d["x"], d["w_gate"], d["w_up"], d["w_down"], out, ws)
 
-    for _ in range(warmup):
-        step()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
-        step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
+    ms, step_ms = timed_steps(step, steps, warmup)
     flops = 6 * cfg.T * cfg.H * cfg.I
     bytes_ = 3 * cfg.I * cfg.H * 2 + cfg.T * cfg.H * 2 + cfg.T * cfg.H * 4
     del d, ws, out
+    torch.cuda.empty_cache()
     return {"tokens": cfg.T, "hidden": cfg.H, "intermediate": cfg.I, "ms_per_step": round(ms, 4),
-            "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
+            **step_stats(step_ms), "tokens_per_s": round(cfg.T / (ms * 1e-3), 1),
             "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
             "roofline": {"bound": "mfma", "achieved": round(flops / (ms * 1e-3) / 1e12, 1),
                          "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                          "frac": round(flops / (ms * 1e-3) / PEAK_BF16, 4), "traffic": None,
                          "algorithmic_bytes": bytes_, "algorithmic_flops": flops}}
+
+
+def achievable_peaks(repeats=5):
+    """What this GPU sustains, measured with the library's measurement kernels
+    (include/moe_peak.h): a streaming read of 8 GiB (far larger than the
+    256 MB Infinity Cache) over several grid sizes, with and without the
+    nontemporal cache policy, and back-to-back bf16 MFMAs on register operands
+    over several grid sizes.  The best rate of each is reported."""
+    import torch
+
+    from group_limited_routing_router_amd import moe
+
+    nbytes = 8 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x5A)
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+
+    def best_ms(fn):
+        fn()
+        times = []
+        for _ in range(repeats):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        return min(times)
+
+    reads = {}
+    for nt in (False, True):
+        for wg in (1024, 2048, 4096, 8192):
+            ms = best_ms(lambda: moe.moe_peak_stream_read(buf, sink, wg, nontemporal=nt))
+            reads[f"{'nt' if nt else 'cached'}_wg{wg}"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf, sink
+    torch.cuda.empty_cache()
+    mfma = {}
+    iters = 20000
+    for wg in (1024, 2048):
+        out = torch.empty(4 * wg, dtype=torch.float32, device="cuda")
+        flops = moe.moe_peak_mfma_bf16(iters, out, wg)  # also the warm-up call
+        ms = best_ms(lambda: moe.moe_peak_mfma_bf16(iters, out, wg))
+        mfma[f"wg{wg}"] = round(flops / (ms * 1e-3) / 1e12, 1)
+        del out
+    hbm = max(reads.values())
+    tf = max(mfma.values())
+    log("[bench] achievable: read %s GB/s, bf16 MFMA %s TFLOP/s" % (reads, mfma))
+    return {"achievable_hbm_gbs": hbm, "achievable_hbm_frac_of_peak": round(hbm * 1e9 / PEAK_HBM, 4),
+            "achievable_mfma_tflops": tf,
+            "achievable_mfma_frac_of_peak": round(tf * 1e12 / PEAK_BF16, 4),
+            "read_gbs_by_grid": reads, "mfma_tflops_by_grid": mfma,
+            "how": "moe_peak_stream_read: one read of 8 GiB, 16-byte loads, 8 in flight per lane, "
+                   "256-thread workgroups; moe_peak_mfma_bf16: 8 independent 32x32x16 bf16 "
+                   f"MFMA chains per wave, {iters} steps, 4 waves per workgroup; best of "
+                   f"{repeats} event-timed calls per grid"}
 
 
 def gemm_study(weights, steps, warmup):
@@ -326,47 +428,57 @@ def roofline_for(res, kernel):
     return r
 
 
-def cpu_baseline(res, target_s):
-    """The oracle, as it stands, on a bounded sample of the timed workload's
-    tokens (routing + expert FFN + combine for the first n tokens)."""
-    import numpy as np
+def cpu_baseline(weights, main_name, target_s):
+    """The oracle, as it stands, timed on this host's cores (the threads of
+    the process affinity mask, OMP_PROC_BIND=close): routing, the expert FFN of
+    every pair and the combine of the first n tokens of a workload.  Every
+    decode token; the first tokens of prefill and skew, sized from the decode
+    rate so the whole takes about target_s; long extrapolated from the prefill
+    rate (the oracle's cost per token does not depend on the routing: k pairs
+    per token).  The weights are copied to the host once, untimed."""
     import torch
 
     if "OMP_NUM_THREADS" not in os.environ:
         os.environ["OMP_NUM_THREADS"] = str(len(os.sched_getaffinity(0)))
     os.environ.setdefault("OMP_PROC_BIND", "close")
     import oracle
-    from group_limited_routing_router_amd.inputs import bits
+    from group_limited_routing_router_amd.inputs import CONFIGS, bits, make_tokens
 
     threads = oracle.num_threads()
+    wh = {k: bits(v) for k, v in weights.items()}
 
-    cfg, d = res["cfg"], res["inputs"]
-    wr = bits(d["w_router"])
-    bias = d["bias"].cpu().numpy()
-
-    def run(n):
+    def run(cfg, n):
+        d = make_tokens(cfg, seed=0, device="cuda")
         xs = bits(d["x"][:n])
+        bias = d["bias"].cpu().numpy()
+        del d
+        torch.cuda.empty_cache()
         t0 = time.perf_counter()
-        ids, w, _, _ = oracle.route(xs, wr, bias, cfg.G, cfg.TG, cfg.k)
-        t_route = time.perf_counter() - t0
-        used = np.unique(ids)
-        sel = torch.from_numpy(used).cuda()
-        wg = bits(d["w_gate"].index_select(0, sel))       # host copies: not timed
-        wu = bits(d["w_up"].index_select(0, sel))
-        wd = bits(d["w_down"].index_select(0, sel))
-        remap = np.full(cfg.E, -1, np.int32)
-        remap[used] = np.arange(len(used), dtype=np.int32)
-        t1 = time.perf_counter()
-        oracle.forward_with_routing(xs, remap[ids], w, wg, wu, wd, cfg.scale)
-        t_ffn = time.perf_counter() - t1
-        return t_route + t_ffn
+        ids, w, _, _ = oracle.route(xs, wh["w_router"], bias, cfg.G, cfg.TG, cfg.k)
+        oracle.forward_with_routing(xs, ids, w, wh["w_gate"], wh["w_up"], wh["w_down"], cfg.scale)
+        return time.perf_counter() - t0
 
-    # calibrate on enough tokens to keep every thread busy (a handful of
-    # tokens gives too few pairs and overstates the per-token time)
-    n0 = max(16, threads // 4)
-    t0 = run(n0)
-    n = int(max(4, min(cfg.T, round(target_s / max(t0 / n0, 1e-6)))))
-    t = run(n)
+    def entry(cfg, n, t):
+        flops = n * (2 * cfg.H * cfg.E + cfg.k * 6 * cfg.H * cfg.I)
+        return {"tokens": n, "of_tokens": cfg.T, "seconds": round(t, 2),
+                "tokens_per_s": round(n / t, 2), "gflops": round(flops / t / 1e9, 1),
+                "full_workload_s": round(t * cfg.T / n, 1)}
+
+    out = {}
+    dec = CONFIGS["decode"]
+    t = run(dec, dec.T)
+    out["decode"] = entry(dec, dec.T, t)
+    rate = dec.T / t
+    for name, share in (("prefill", 0.6), ("skew", 0.25)):
+        cfg = CONFIGS[name]
+        n = int(max(64, min(cfg.T, round(rate * target_s * share))))
+        out[name] = entry(cfg, n, run(cfg, n))
+    lg, pre = CONFIGS["long"], out["prefill"]
+    out["long"] = {"tokens": 0, "of_tokens": lg.T, "extrapolated": True,
+                   "tokens_per_s": pre["tokens_per_s"], "gflops": pre["gflops"],
+                   "full_workload_s": round(lg.T / pre["tokens_per_s"], 1),
+                   "note": "not run: the prefill sample's rate applied to 65536 tokens"}
+    del wh
     model = ""
     try:
         with open("/proc/cpuinfo") as f:
@@ -376,10 +488,211 @@ def cpu_baseline(res, target_s):
                     break
     except OSError:
         pass
-    return dict(value=round(n / t, 2), unit="tokens/s", cores=threads, kind="oracle",
-                sample=f"first {n} of the {cfg.T} tokens of the {cfg.name} workload: "
-                       f"routing, expert FFN and combine ({t:.1f} s)",
-                cpu_model=model)
+    main = out[main_name]
+    return dict(value=main["tokens_per_s"], unit="tokens/s", cores=threads, kind="oracle",
+                sample=f"{main['tokens']} of the {main['of_tokens']} tokens of the {main_name} "
+                       f"workload (routing, expert FFN, combine) in {main['seconds']} s"
+                       if not main.get("extrapolated") else
+                       f"the {main_name} rate extrapolated from the prefill sample",
+                cpu_model=model, workloads=out)
+
+
+# ---- rocprofv3 output summaries -----------------------------------------
+
+def _csv_files(path, suffix):
+    if os.path.isdir(path):
+        files = sorted(glob.glob(os.path.join(path, "**", "*" + suffix), recursive=True))
+    else:
+        files = [path]
+    if not files:
+        raise SystemExit(f"no *{suffix} under {path}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            rows += list(csv.DictReader(f))
+    return rows
+
+
+def short_kernel_name(name):
+    """'void moe::(anonymous namespace)::ffn_gemm_dma_kernel<true, false>(...)'
+    -> 'ffn_gemm_dma_kernel<true, false>'."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):  # drop the parameter list
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0 and not name[i:].startswith("(anonymous"):
+            cut = i
+            break
+    name = name[:cut]
+    name = re.sub(r"\(anonymous namespace\)::", "", name)
+    name = re.sub(r"^(\w+::)+", "", name)
+    return re.sub(r"\b(moe|std)::", "", name)
+
+
+def step_of(kname):
+    """The block's step a kernel belongs to (fp8_* for the FP8-weight GEMMs)."""
+    if kname.startswith("route"):
+        return "route"
+    if kname.startswith("permute") or kname.startswith("identity_dispatch"):
+        return "permute"
+    if kname.startswith("combine_residual"):
+        return "combine_residual"
+    if kname.startswith("combine"):
+        return "combine"
+    if kname.startswith("ffn_gemm"):
+        flags = re.findall(r"\b(true|false)\b", kname)
+        gateup = flags[0] == "true"
+        fp8 = len(flags) > 1 and flags[1] == "true"
+        return ("fp8_" if fp8 else "") + ("gate_up" if gateup else "down")
+    return "other"
+
+
+def _grid(row):
+    for k in ("Grid_Size", "Grid_Size_X"):
+        if k in row and row[k]:
+            return int(row[k])
+    return 0
+
+
+def summarize_trace(path, skip):
+    """Per kernel: launches after the first `skip` of each kernel name,
+    average / median / min / max duration in microseconds."""
+    rows = _csv_files(path, "kernel_trace.csv")
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    by = {}
+    for r in rows:
+        k = short_kernel_name(r["Kernel_Name"])
+        by.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"]), _grid(r)))
+    lines = [f"# skipped: the first {skip} launches of each kernel",
+             "# step               kernel                                             grid  calls"
+             "    avg_us    med_us    min_us    max_us"]
+    for k, v in sorted(by.items(), key=lambda kv: STEPS.index(step_of(kv[0]).replace("fp8_", ""))
+                       if step_of(kv[0]).replace("fp8_", "") in STEPS else 99):
+        d = [x[0] / 1e3 for x in v[skip:]] or [x[0] / 1e3 for x in v]
+        lines.append(f"  {step_of(k):<18} {k:<48} {v[0][1]:>9} {len(d):>6} {sum(d) / len(d):>9.1f} "
+                     f"{statistics.median(d):>9.1f} {min(d):>9.1f} {max(d):>9.1f}")
+    print("\n".join(lines))
+
+
+def _per_dispatch(rows, counter):
+    """{dispatch id: (short kernel name, grid, counter value summed over its
+    rows)} for one counter of a rocprofv3 --pmc run, in dispatch order."""
+    out = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        did = int(r["Dispatch_Id"])
+        k = short_kernel_name(r["Kernel_Name"])
+        prev = out.get(did, (k, _grid(r), 0.0))
+        out[did] = (k, prev[1], prev[2] + float(r["Counter_Value"]))
+    return dict(sorted(out.items()))
+
+
+def summarize_pmc(fetch_path, write_path, skip, workload=None, update=False):
+    """HBM bytes per launch from a FETCH_SIZE run and a WRITE_SIZE run (KiB per
+    dispatch), each scaled by what the same counter reads for the plain 1 GiB
+    device copy the runs make (--copy-calibration): bytes = FETCH_SIZE x
+    (2^30 / 1024 / copy FETCH_SIZE) x 1024, the same for WRITE_SIZE.  Averaged
+    per kernel over the launches after the first `skip`; with --update-traffic
+    the per-step sums go to profiles/traffic.json under the workload's name,
+    keyed to the hash of the kernel sources."""
+    fd = _per_dispatch(_csv_files(fetch_path, "counter_collection.csv"), "FETCH_SIZE")
+    wd = _per_dispatch(_csv_files(write_path, "counter_collection.csv"), "WRITE_SIZE")
+    copy_f = [v for v in fd.values() if "copyBuffer" in v[0]]
+    copy_w = [v for v in wd.values() if "copyBuffer" in v[0]]
+    if not copy_f or not copy_w:
+        raise SystemExit("no device copy in the runs: profile with --copy-calibration")
+    cf, cw = max(c[2] for c in copy_f), max(c[2] for c in copy_w)
+    ff, wf = (1 << 30) / 1024 / cf, (1 << 30) / 1024 / cw
+
+    def per_kernel(d):
+        by = {}
+        for k, g, v in d.values():
+            if "copyBuffer" in k or "fill" in k.lower() or k.startswith("at::"):
+                continue
+            by.setdefault(k, []).append((g, v))
+        return {k: (v[0][0], [x[1] for x in v[skip:]] or [x[1] for x in v]) for k, v in by.items()}
+
+    fk, wk = per_kernel(fd), per_kernel(wd)
+    lines = [f"# calibration: the 1 GiB device copy reads FETCH_SIZE={cf:.0f} KiB and "
+             f"WRITE_SIZE={cw:.0f} KiB;",
+             f"#   HBM bytes = FETCH_SIZE x {ff:.3f} x 1024 + WRITE_SIZE x {wf:.3f} x 1024",
+             f"# skipped: the first {skip} launches of each kernel",
+             "# step               kernel                                             grid"
+             "    FETCH_KiB  WRITE_KiB  read_GB write_GB"]
+    steps = {}
+    for k in sorted(fk, key=lambda n: STEPS.index(step_of(n).replace("fp8_", ""))
+                    if step_of(n).replace("fp8_", "") in STEPS else 99):
+        fv = sum(fk[k][1]) / len(fk[k][1])
+        wv = sum(wk.get(k, (0, [0.0]))[1]) / max(1, len(wk.get(k, (0, [0.0]))[1]))
+        rb, wb = fv * ff * 1024, wv * wf * 1024
+        st = step_of(k)
+        s = steps.setdefault(st, {"fetch_bytes": 0, "write_bytes": 0})
+        s["fetch_bytes"] += int(rb)
+        s["write_bytes"] += int(wb)
+        lines.append(f"  {st:<18} {k:<48} {fk[k][0]:>9} {fv:>12.0f} {wv:>10.0f} {rb / 1e9:>8.3f} "
+                     f"{wb / 1e9:>8.3f}")
+    print("\n".join(lines))
+    if update:
+        try:
+            with open(TRAFFIC_FILE) as f:
+                tr = json.load(f)
+        except (OSError, ValueError):
+            tr = {}
+        sha = kernel_source_sha()
+        if tr.get("kernel_source_sha") != sha:
+            tr = {"kernel_source_sha": sha}
+        tr["fetch_factor"], tr["write_factor"] = ff, wf
+        tr.setdefault(workload, {}).update(steps)
+        with open(TRAFFIC_FILE, "w") as f:
+            json.dump(tr, f, indent=1)
+        log(f"[bench] traffic of {workload} stored under kernel sources {sha}")
+
+
+def kernels_only(args, weights):
+    """The timed workload's steps as separate calls only (warmup + steps
+    launches of each kernel, nothing else on the GPU), optionally with the
+    FP8 expert FFN, a plain 1 GiB device copy for counter calibration, and
+    the event times of this same run."""
+    import torch
+
+    from group_limited_routing_router_amd import moe
+    from group_limited_routing_router_amd.inputs import CONFIGS, make_weights_fp8
+
+    if args.copy_calibration:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        bb = torch.empty_like(a)
+        for _ in range(3):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+        del a, bb
+    res = run_workload(args.workload, args.steps, args.warmup, weights, forward=False)
+    line = {"mode": "kernels-only", "workload": f"beam-moe-{args.workload}", "steps": args.steps,
+            "warmup": args.warmup,
+            "kernels_ms": {k: round(v, 4) for k, v in res["kernel_ms"].items()},
+            "roofline": roofline_for(res, "gate_up")}
+    if args.with_fp8:
+        cfg, b, d = res["cfg"], res["buffers"], res["inputs"]
+        for k in ("w_gate", "w_up", "w_down"):
+            d.pop(k, None)
+        weights.clear()
+        torch.cuda.empty_cache()
+        w8 = make_weights_fp8(CONFIGS["decode"], seed=0, device="cuda")
+        p = moe.MoEProblem.from_config(cfg)
+
+        def ffn8():
+            moe.moe_expert_ffn_fp8(p, d["x"], b["sorted_pairs"], b["expert_offsets"], w8["q_gate"],
+                                   w8["s_gate"], w8["q_up"], w8["s_up"], w8["q_down"],
+                                   w8["s_down"], b["y"], b["ws"])
+
+        ms, _ = timed_steps(ffn8, args.steps, args.warmup)
+        line["fp8_expert_ffn_ms"] = round(ms, 4)
+    print(json.dumps(line), flush=True)
 
 
 def main():
@@ -389,12 +702,14 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "decode", "skew", "long"])
-    ap.add_argument("--no-decode", action="store_true",
-                    help="skip the secondary decode (T=128) measurement")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the secondary decode, skew and long measurements")
     ap.add_argument("--no-fp8", action="store_true",
                     help="skip the secondary FP8-weight measurements")
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the secondary dense-MLP measurement")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the achievable-peak measurement kernels")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -402,6 +717,18 @@ def main():
     ap.add_argument("--gemm-study", action="store_true",
                     help="instead of the benchmark: the prefill expert GEMMs at fixed rows per "
                          "expert next to the library batched GEMM (one JSON line)")
+    ap.add_argument("--kernels-only", action="store_true",
+                    help="instead of the benchmark: the workload's steps as separate calls only")
+    ap.add_argument("--with-fp8", action="store_true",
+                    help="with --kernels-only: also the FP8-weight expert FFN")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print per-kernel durations of a rocprofv3 kernel trace (no GPU)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print HBM bytes per launch from two rocprofv3 --pmc runs (no GPU)")
+    ap.add_argument("--skip", type=int, default=0,
+                    help="with --summarize-*: leave out the first N launches of each kernel")
+    ap.add_argument("--update-traffic", action="store_true",
+                    help="with --summarize-pmc: store the figures for --workload")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -409,6 +736,12 @@ def main():
         print("bench.py measures one GPU only: this build has no multi-GPU path "
               "(run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.skip)
+        return
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc, args.skip, args.workload, args.update_traffic)
+        return
 
     import torch
 
@@ -422,6 +755,9 @@ def main():
     if args.gemm_study:
         gemm_study(weights, args.steps, args.warmup)
         return
+    if args.kernels_only:
+        kernels_only(args, weights)
+        return
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
@@ -431,6 +767,7 @@ def main():
         torch.cuda.synchronize()
         del a, bb
 
+    peaks = None if args.no_peaks else achievable_peaks()
     main_res = run_workload(args.workload, args.steps, args.warmup, weights)
     cfg = main_res["cfg"]
     kms = main_res["kernel_ms"]
@@ -441,12 +778,13 @@ def main():
     ms = main_res["ms"]
     out = {
         "metric": "MoE-layer tokens/s + % bf16 MFMA peak (T=8192); % HBM peak BW (T=128)",
-        "value": round(cfg.T * args.steps / (ms * 1e-3 * args.steps), 1),
+        "value": round(cfg.T / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        **step_stats(main_res["step_ms"]),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -456,33 +794,32 @@ def main():
                    "intermediate": cfg.I, "experts": cfg.E, "groups": cfg.G,
                    "kept_groups": cfg.TG, "top_k": cfg.k, "scale": cfg.scale,
                    "experts_hit": main_res["n_hit"]},
-        "layer": {"tflops": round(layer["flops"] / (ms * 1e-3) / 1e12, 1),
-                  "mfma_frac": round(layer["flops"] / (ms * 1e-3) / PEAK_BF16, 4),
-                  "hbm_gbs": round(layer["bytes"] / (ms * 1e-3) / 1e9, 1),
-                  "hbm_frac": round(layer["bytes"] / (ms * 1e-3) / PEAK_HBM, 4)},
+        "layer": {k: v for k, v in workload_summary(main_res, peaks).items()
+                  if k in ("tflops", "mfma_frac", "hbm_gbs", "hbm_frac", "mfma_frac_of_achievable",
+                           "hbm_frac_of_achievable", "hot_expert_share")},
         "kernels_ms": {k: round(v, 4) for k, v in kms.items() if k != "combine_residual"},
         "roofline": roofline_for(main_res, dominant),
         # the combine fused with the post-norm and residual update (not part of
         # the timed step: a separate entry point after the block)
         "combine_residual": roofline_for(main_res, "combine_residual"),
     }
-    if not args.no_decode and args.workload != "decode":
-        dec = run_workload("decode", args.steps, args.warmup, weights)
-        dl = dec["layer"]
-        out["decode"] = {
-            "tokens": dec["cfg"].T, "ms_per_step": round(dec["ms"], 4),
-            "tokens_per_s": round(dec["cfg"].T / (dec["ms"] * 1e-3), 1),
-            "experts_hit": dec["n_hit"],
-            "hbm_gbs": round(dl["bytes"] / (dec["ms"] * 1e-3) / 1e9, 1),
-            "hbm_frac": round(dl["bytes"] / (dec["ms"] * 1e-3) / PEAK_HBM, 4),
-            "kernels_ms": {k: round(v, 4) for k, v in dec["kernel_ms"].items()
-                           if k != "combine_residual"},
-            "roofline": roofline_for(dec, max((k for k in dec["kernel_ms"] if k != "combine_residual"),
-                                              key=dec["kernel_ms"].get)),
-        }
-        log("[bench] decode T=128: %.3f ms/step, %.1f%% of HBM peak" % (
-            dec["ms"], 100 * out["decode"]["hbm_frac"]))
-        del dec
+    if peaks:
+        out["achievable_hbm_gbs"] = peaks["achievable_hbm_gbs"]
+        out["achievable_mfma_tflops"] = peaks["achievable_mfma_tflops"]
+        out["achievable"] = peaks
+    del main_res
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        for name in ("decode", "skew", "long"):
+            if name == args.workload:
+                continue
+            r = run_workload(name, args.steps, args.warmup, weights)
+            out[name] = workload_summary(r, peaks)
+            log("[bench] %s T=%d: %.3f ms/step, %.1f%% of bf16 MFMA peak, %.1f%% of HBM peak" % (
+                name, r["cfg"].T, r["ms"], 100 * out[name]["mfma_frac"],
+                100 * out[name]["hbm_frac"]))
+            del r
+            torch.cuda.empty_cache()
     if not args.no_fp8:
         from group_limited_routing_router_amd.inputs import make_weights_fp8
         w8 = make_weights_fp8(CONFIGS["decode"], seed=0, device="cuda")
@@ -498,7 +835,7 @@ def main():
             out["dense_mlp"]["tokens"], out["dense_mlp"]["intermediate"],
             out["dense_mlp"]["ms_per_step"], 100 * out["dense_mlp"]["roofline"]["frac"]))
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(main_res, args.cpu_seconds)
+        out["cpu_baseline"] = cpu_baseline(weights, args.workload, args.cpu_seconds)
         log("[bench] cpu oracle: %s" % out["cpu_baseline"])
     print(json.dumps(out), flush=True)
 

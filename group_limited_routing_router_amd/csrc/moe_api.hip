@@ -34,6 +34,7 @@ moe_status ok() {
 }
 
 constexpr size_t kAlign = 256;
+constexpr int kMaxDim = 65536;  // largest H and I the kernels take
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
@@ -78,6 +79,10 @@ moe_status check_problem(const moe_problem* p) {
     if (p->E > 256) return fail(MOE_ERR_UNSUPPORTED, "E=%d > 256", p->E);
     if (p->k > 16) return fail(MOE_ERR_UNSUPPORTED, "k=%d > 16", p->k);
     if (p->H % 128 != 0) return fail(MOE_ERR_UNSUPPORTED, "H=%d is not a multiple of 128", p->H);
+    // the expert GEMMs form 32-bit byte offsets within one tile's rows of a
+    // weight matrix, h or y (at most 256 rows x 65536 x 4 bytes)
+    if (p->H > kMaxDim) return fail(MOE_ERR_UNSUPPORTED, "H=%d > %d", p->H, kMaxDim);
+    if (p->I > kMaxDim) return fail(MOE_ERR_UNSUPPORTED, "I=%d > %d", p->I, kMaxDim);
     return MOE_OK;
 }
 

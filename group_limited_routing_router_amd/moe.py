@@ -51,7 +51,9 @@ class MoEProblem(ctypes.Structure):
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
            "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_combine_residual",
            "moe_dense_mlp", "moe_expert_ffn_fp8", "moe_forward", "moe_forward_fp8",
-           "moe_status_string", "moe_last_error")
+           "moe_status_string", "moe_last_error",
+           # measurement kernels (include/moe_peak.h)
+           "moe_peak_stream_read", "moe_peak_mfma_bf16", "moe_peak_mfma_bf16_flops")
 
 
 def library_path() -> str:
@@ -115,6 +117,12 @@ def load_library():
         lib.moe_forward.argtypes = [prob, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, P,
                                     ctypes.c_size_t, P]
         lib.moe_forward.restype = st
+        lib.moe_peak_stream_read.argtypes = [P, ctypes.c_size_t, ctypes.c_int, P, ctypes.c_int, P]
+        lib.moe_peak_stream_read.restype = st
+        lib.moe_peak_mfma_bf16.argtypes = [ctypes.c_int64, P, ctypes.c_int, P]
+        lib.moe_peak_mfma_bf16.restype = st
+        lib.moe_peak_mfma_bf16_flops.argtypes = [ctypes.c_int64, ctypes.c_int]
+        lib.moe_peak_mfma_bf16_flops.restype = ctypes.c_double
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         lib.moe_last_error.argtypes = []
@@ -232,6 +240,22 @@ def moe_forward(p, x, w_router, bias, w_gate, w_up, w_down, out, topk_ids, topk_
                                        _p(w_up), _p(w_down), _p(out), _dtype_code(out),
                                        _p(topk_ids), _p(topk_weights), _p(y), _p(ws), nbytes,
                                        _stream(stream)))
+
+
+def moe_peak_stream_read(buf, sink, workgroups, nontemporal=False, stream=None):
+    """One streaming read of the whole of `buf` (a GPU tensor) by the
+    measurement kernel; `sink` is a GPU tensor of at least 4 bytes."""
+    nbytes = buf.numel() * buf.element_size()
+    _check(load_library().moe_peak_stream_read(_p(buf), nbytes, int(bool(nontemporal)), _p(sink),
+                                                int(workgroups), _stream(stream)))
+
+
+def moe_peak_mfma_bf16(iters, sink, workgroups, stream=None):
+    """The back-to-back bf16 MFMA loop; `sink` holds 4 * workgroups floats.
+    Returns the FLOPs of the call."""
+    lib = load_library()
+    _check(lib.moe_peak_mfma_bf16(int(iters), _p(sink), int(workgroups), _stream(stream)))
+    return float(lib.moe_peak_mfma_bf16_flops(int(iters), int(workgroups)))
 
 
 def alloc_buffers(p: MoEProblem, device="cuda", out_dtype=torch.float32):

@@ -63,8 +63,9 @@ typedef enum moe_dtype { MOE_DTYPE_F32 = 0, MOE_DTYPE_BF16 = 1 } moe_dtype;
 
 /* Problem shape.
  *   T  tokens (>= 0; T = 0 is a no-op that returns MOE_OK)
- *   H  hidden size,        H % 64 == 0 (H % 128 == 0 for the kernels)
- *   I  expert intermediate size, I % 64 == 0
+ *   H  hidden size,        H % 64 == 0 (H % 128 == 0 and H <= 65536 for the
+ *      kernels, else MOE_ERR_UNSUPPORTED)
+ *   I  expert intermediate size, I % 64 == 0 (I <= 65536 for the kernels)
  *   E  experts, 1 <= E <= 256
  *   G  groups, E % G == 0; group g holds experts [g*E/G, (g+1)*E/G)
  *   TG kept groups, 1 <= TG <= G
@@ -82,7 +83,10 @@ typedef struct moe_problem {
  * workspace sized by this function serves every call. */
 size_t moe_workspace_bytes(const moe_problem* p);
 
-/* Router and group-limited selection for T tokens.
+/* Router and group-limited selection for T tokens ("Welcome Beam: a 501B open
+ * model you can own, customize, and scale", section "Mixture of Experts": a
+ * sigmoid score per expert, groups ranked by their two best scores, the best
+ * groups kept, the top k experts of those groups, normalised weights).
  *   x            [T,H] bf16 activations
  *   w_router     [E,H] bf16 router weight
  *   bias         [E] fp32 added to each logit before the sigmoid, or NULL (0)
@@ -93,7 +97,9 @@ moe_status moe_route(const moe_problem* p, const moe_bf16* x, const moe_bf16* w_
                      const float* bias, int32_t* topk_ids, float* topk_weights,
                      hipStream_t stream);
 
-/* Dispatch: stable counting sort of the T*k pairs p = t*k + j by expert.
+/* Dispatch: stable counting sort of the T*k pairs p = t*k + j by expert (the
+ * same section: only the k chosen experts run on a token, so each expert's
+ * tokens are gathered into one contiguous run of rows).
  *   topk_ids       [T,k] int32 in: expert of each pair, 0 <= id < E
  *   expert_offsets [E+1] int32 out: first sorted position of each expert;
  *                  expert_offsets[E] = T*k
@@ -106,7 +112,8 @@ moe_status moe_permute(const moe_problem* p, const int32_t* topk_ids, int32_t* e
                        int32_t* sorted_pairs, int32_t* pair_rows, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
-/* Expert SwiGLU MLPs over the sorted pairs.
+/* Expert SwiGLU MLPs over the sorted pairs (the same section: every expert is
+ * a SwiGLU MLP; section "Residual Stream": the SwiGLU product in FP32).
  *   x              [T,H] bf16; row of pair q is x[sorted_pairs[q] / k]
  *   sorted_pairs, expert_offsets   as written by moe_permute
  *   w_gate, w_up   [E,I,H] bf16;  w_down [E,H,I] bf16
@@ -136,7 +143,8 @@ moe_status moe_expert_gate_up(const moe_problem* p, const moe_bf16* x, const int
 moe_status moe_expert_down(const moe_problem* p, const moe_bf16* h, const int32_t* expert_offsets,
                            const moe_bf16* w_down, float* y, hipStream_t stream);
 
-/* Weighted recombination without atomics.
+/* Weighted recombination without atomics (the same section: the expert outputs
+ * are summed with the normalised router weights and scaled by 2.5 for Beam).
  *   y            [T*k,H] fp32 in sorted order
  *   pair_rows    [T*k] int32 (from moe_permute); -1 entries contribute 0
  *   topk_weights [T,k] fp32
@@ -209,7 +217,8 @@ moe_status moe_forward_fp8(const moe_problem* p, const moe_bf16* x, const moe_bf
                            int32_t* topk_ids, float* topk_weights, float* y, void* ws,
                            size_t ws_bytes, hipStream_t stream);
 
-/* The whole block: route, permute, expert FFN, combine.
+/* The whole block: route, permute, expert FFN, combine ("Welcome Beam: a 501B
+ * open model you can own, customize, and scale", section "Mixture of Experts").
  *   topk_ids, topk_weights  optional [T,k] outputs (NULL: kept in `ws`)
  *   y                       [T*k,H] fp32 caller buffer for expert outputs
  *   out                     [T,H] in out_dtype

@@ -1,0 +1,50 @@
+/*
+ * moe_peak.h -- measurement kernels of libmoe.so that anchor the roofline.
+ *
+ * They are not part of the MoE block: they measure what this GPU sustains
+ * for the two resources the block's kernels are bound by, a streaming read
+ * from HBM (the weight stream of the expert GEMMs at decode) and back-to-back
+ * bf16 MFMAs (the expert GEMMs at prefill), so the block's rates can be
+ * reported against these achievable figures next to the published peaks.
+ *
+ * Same conventions as moe.h: caller-owned device memory, nothing allocated or
+ * synchronised, work only enqueued on `stream`; arguments are checked on the
+ * host first and nothing is enqueued on an error.  The time is the caller's
+ * to take (events around the call).
+ */
+#ifndef MOE_PEAK_H
+#define MOE_PEAK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Reads `bytes` bytes of `buf` once, with 16-byte loads spread over
+ * `workgroups` workgroups of 256 threads (8 loads in flight per thread,
+ * consecutive lanes on consecutive 16-byte chunks), nontemporal loads if
+ * `nontemporal` is nonzero.  Writes at most one 32-bit value to sink[0] (and
+ * almost never: only if the XOR of the buffer equals a fixed key).
+ *   buf    16-byte aligned; bytes a positive multiple of 16
+ * MOE_ERR_INVALID_ARG on a bad argument, MOE_ERR_HIP if the launch fails. */
+moe_status moe_peak_stream_read(const void* buf, size_t bytes, int nontemporal, uint32_t* sink,
+                                int workgroups, hipStream_t stream);
+
+/* Every wave of `workgroups` workgroups of 256 threads (4 waves) runs `iters`
+ * steps of 8 independent 32x32x16 bf16 MFMAs on register operands (no memory
+ * traffic), then writes one float: sink[wave index], sink holding
+ * 4 * workgroups floats.  moe_peak_mfma_bf16_flops gives the FLOPs of one
+ * call (2 * 32 * 32 * 16 per MFMA). */
+moe_status moe_peak_mfma_bf16(int64_t iters, float* sink, int workgroups, hipStream_t stream);
+
+double moe_peak_mfma_bf16_flops(int64_t iters, int workgroups);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_PEAK_H */

@@ -79,3 +79,90 @@ def out_error(gpu_out, ref_out):
     err = np.abs(gpu_out.astype(np.float64) - ref)
     rms = float(np.sqrt(np.mean(ref ** 2)))
     return float(err.max()) / rms if rms > 0 else float(err.max()), rms
+
+
+# ---- unwritten-output detection ----------------------------------------
+#
+# Every output buffer is prefilled with a value no call writes (NaN for
+# floating-point outputs, -1 for indices, 0xFF bytes -- a bf16 NaN -- for the
+# workspace), so a tile, row or token that a kernel skips shows up as a
+# surviving sentinel instead of a stale correct value left by an earlier call.
+
+def fill_sentinels(bufs):
+    """Fill every tensor of a buffer dict (moe.alloc_buffers) in place."""
+    import torch
+    for v in bufs.values():
+        if v.dtype in (torch.float32, torch.bfloat16):
+            v.fill_(float("nan"))
+        elif v.dtype == torch.int32:
+            v.fill_(-1)
+        elif v.dtype == torch.uint8:
+            v.fill_(0xFF)
+        else:
+            raise TypeError(v.dtype)
+    return bufs
+
+
+def sentinel_buffers(moe, p, out_dtype=None):
+    """moe.alloc_buffers(p) with every buffer holding its sentinel."""
+    import torch
+    b = moe.alloc_buffers(p, out_dtype=out_dtype or torch.float32)
+    return fill_sentinels(b)
+
+
+def all_finite(t, rows_per_chunk=1 << 16):
+    """True if every element of a (possibly many-GB) GPU tensor is finite;
+    checked on the GPU in row chunks."""
+    import torch
+    for c in torch.split(t, rows_per_chunk):
+        if not bool(torch.isfinite(c).all()):
+            return False
+    return True
+
+
+def assert_forward_written(b, P, E, out=True, y=True):
+    """After a forward pass with every pair kept: no sentinel survives in
+    out, y (all P rows), topk_ids (all in [0, E)) or topk_weights."""
+    import torch
+    ids = b["topk_ids"]
+    assert int(ids.min()) >= 0 and int(ids.max()) < E, "unwritten or invalid expert id"
+    assert bool(torch.isfinite(b["topk_weights"]).all()), "unwritten routing weight"
+    if y:
+        assert all_finite(b["y"][:P]), "unwritten row of y"
+    if out:
+        assert all_finite(b["out"]), "unwritten element of out"
+
+
+def edge_rows(off, n_extra_per_split=(191, 192, 255, 256), big=512):
+    """Sorted positions at the edges of the expert GEMMs' row tiles, for
+    sampling: the first and last row of every expert; for experts with more
+    than 256 rows (split into several row tiles) the rows on either side of
+    the 192- and 256-row marks; for experts with more than `big` rows every
+    256-row boundary.  Returns a sorted array of positions."""
+    off = np.asarray(off, np.int64)
+    q = []
+    for e in range(off.size - 1):
+        a, n = int(off[e]), int(off[e + 1] - off[e])
+        if n == 0:
+            continue
+        q += [a, a + n - 1]
+        if n > 256:
+            q += [a + m for m in n_extra_per_split if m < n]
+        if n > big:
+            q += [a + m for m in range(255, n, 256)] + [a + m for m in range(256, n, 256)]
+    return np.unique(np.asarray(q, np.int64))
+
+
+def stratified_tokens(off, sorted_pairs, k, T, n, rng, always=()):
+    """About n distinct tokens: those whose pairs sit at the row-tile edges
+    (edge_rows; at most n/2 of them, a seeded choice if there are more), the
+    tokens in `always`, and seeded random tokens for the rest."""
+    edge_tok = np.unique(np.asarray(sorted_pairs, np.int64)[edge_rows(off)] // k)
+    if edge_tok.size > n // 2:
+        edge_tok = np.sort(rng.choice(edge_tok, n // 2, replace=False))
+    chosen = set(edge_tok.tolist()) | {int(t) for t in always}
+    rest = np.setdiff1d(np.arange(T), np.fromiter(chosen, np.int64, len(chosen)))
+    need = max(0, n - len(chosen))
+    if need and rest.size:
+        chosen |= set(rng.choice(rest, min(need, rest.size), replace=False).tolist())
+    return np.array(sorted(chosen), np.int64)

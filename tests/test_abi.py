@@ -9,6 +9,8 @@ import numpy as np
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
 
@@ -20,7 +22,7 @@ def lib():
 
 
 def _declared():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
@@ -55,7 +57,7 @@ def test_workspace_bytes(lib):
 @pytest.mark.parametrize("field,value,status", [
     ("T", -1, 1), ("H", 100, 1), ("H", 0, 1), ("I", 96, 1), ("E", 0, 1), ("G", 7, 1),
     ("TG", 0, 1), ("TG", 9, 1), ("k", 0, 1), ("k", 129, 1), ("E", 512, 1), ("k", 17, 2),
-    ("H", 192, 2),
+    ("H", 192, 2), ("H", 65536 + 128, 2), ("I", 65536 + 64, 2),
 ])
 def test_problem_validation(lib, field, value, status):
     p = _beam()
@@ -179,3 +181,19 @@ def test_header_serves_a_plain_c_program(tmp_path, lib):
     r = subprocess.run([exe], capture_output=True, text=True, timeout=60)
     assert r.returncode == 2 and "usage" in r.stderr
 
+
+
+def test_measurement_kernels_reject_bad_arguments(lib):
+    cdll = lib.load_library()
+    keep, good = _aligned()
+    keep2, odd = _aligned(offset=4)
+    i64 = ctypes.c_int64
+    assert cdll.moe_peak_stream_read(None, 4096, 0, good, 16, None) == 1
+    assert cdll.moe_peak_stream_read(good, 4096, 0, None, 16, None) == 1
+    assert cdll.moe_peak_stream_read(good, 4008, 0, good, 16, None) == 1   # not a multiple of 16
+    assert cdll.moe_peak_stream_read(odd, 4096, 0, good, 16, None) == 1    # misaligned
+    assert cdll.moe_peak_stream_read(good, 4096, 0, good, 0, None) == 1    # no workgroups
+    assert cdll.moe_peak_mfma_bf16(i64(0), good, 16, None) == 1
+    assert cdll.moe_peak_mfma_bf16(i64(10), None, 16, None) == 1
+    # FLOPs of one call: waves x steps x 8 chains x 2*32*32*16
+    assert lib.load_library().moe_peak_mfma_bf16_flops(i64(100), 3) == 3 * 4 * 100 * 8 * 32768

@@ -78,3 +78,53 @@ def test_stored_traffic_layout():
 def test_kernel_source_sha_is_stable():
     assert bench.kernel_source_sha() == bench.kernel_source_sha()
     assert all(p.endswith((".hip", ".h")) for p in bench.KERNEL_SOURCES)
+
+
+def test_kernel_names_and_steps():
+    n = ("void moe::(anonymous namespace)::ffn_gemm_dma_kernel<true, false>"
+         "(moe::(anonymous namespace)::FfnArgs)")
+    assert bench.short_kernel_name(n) == "ffn_gemm_dma_kernel<true, false>"
+    assert bench.step_of("ffn_gemm_dma_kernel<true, false>") == "gate_up"
+    assert bench.step_of("ffn_gemm_dma_kernel<false, true>") == "fp8_down"
+    assert bench.step_of("ffn_gemm_kernel<16, 128, 1, 4, true, false, 128>") == "gate_up"
+    assert bench.step_of("route_small_kernel<8, 1, 10>") == "route"
+    assert bench.step_of("permute_scatter_kernel") == "permute"
+    assert bench.step_of("combine_residual_kernel<8, 8>") == "combine_residual"
+    assert bench.step_of("combine_kernel<8, false>") == "combine"
+
+
+def _write_csv(path, header, rows):
+    import csv
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        w = csv.writer(f)
+        w.writerow(header)
+        w.writerows(rows)
+
+
+def test_trace_and_counter_summaries(tmp_path, capsys):
+    gu = "void moe::(anonymous namespace)::ffn_gemm_dma_kernel<true, false>(FfnArgs)"
+    cp = "__amd_rocclr_copyBuffer"
+    # kernel trace: 3 launches of gate_up (1000, 2000, 3000 us), skip the first
+    hdr = ["Kind", "Dispatch_Id", "Kernel_Name", "Start_Timestamp", "End_Timestamp", "Grid_Size_X"]
+    rows = [["KERNEL_DISPATCH", i + 1, gu, 10 ** 9 * i, 10 ** 9 * i + 10 ** 6 * (i + 1), 2621440]
+            for i in range(3)]
+    _write_csv(str(tmp_path / "tr" / "host" / "1" / "t_kernel_trace.csv"), hdr, rows)
+    bench.summarize_trace(str(tmp_path / "tr"), skip=1)
+    out = capsys.readouterr().out
+    line = [ln for ln in out.splitlines() if "ffn_gemm_dma_kernel" in ln][0].split()
+    assert line[0] == "gate_up" and line[-5] == "2" and float(line[-4]) == 2500.0
+    # counters: the copy reads half its bytes in FETCH_SIZE units (factor 2)
+    hdr = ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Counter_Name", "Counter_Value"]
+    f_rows = [[1, cp, 1024, "FETCH_SIZE", 524288], [2, gu, 2621440, "FETCH_SIZE", 1000],
+              [3, gu, 2621440, "FETCH_SIZE", 3000]]
+    w_rows = [[1, cp, 1024, "WRITE_SIZE", 1048576], [2, gu, 2621440, "WRITE_SIZE", 10],
+              [3, gu, 2621440, "WRITE_SIZE", 30]]
+    _write_csv(str(tmp_path / "f" / "x_counter_collection.csv"), hdr, f_rows)
+    _write_csv(str(tmp_path / "w" / "x_counter_collection.csv"), hdr, w_rows)
+    bench.summarize_pmc(str(tmp_path / "f"), str(tmp_path / "w"), skip=1)
+    out = capsys.readouterr().out
+    line = [ln for ln in out.splitlines() if "ffn_gemm_dma_kernel" in ln][0].split()
+    # 3000 KiB x 2 -> 6.144 MB read; 30 KiB x 1 -> 0.031 MB written
+    assert abs(float(line[-2]) - 3000 * 2 * 1024 / 1e9) < 1e-3
+    assert "x 2.000 x 1024" in out

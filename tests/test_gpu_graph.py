@@ -8,6 +8,8 @@ import torch
 
 from group_limited_routing_router_amd.inputs import MoEConfig, make_inputs, make_weights_fp8
 
+from _parity import assert_forward_written, sentinel_buffers
+
 pytestmark = pytest.mark.gpu
 
 
@@ -35,7 +37,7 @@ def test_forward_replays_from_a_graph(moe, shape, fp8):
     d = {n: v.cuda() for n, v in make_inputs(cfg, seed=5).items()}
     w8 = make_weights_fp8(cfg, seed=5, device="cuda") if fp8 else None
     p = moe.MoEProblem.from_config(cfg)
-    b = moe.alloc_buffers(p)
+    b = sentinel_buffers(moe, p)
 
     def forward():
         if fp8:
@@ -48,6 +50,7 @@ def test_forward_replays_from_a_graph(moe, shape, fp8):
 
     forward()
     torch.cuda.synchronize()
+    assert_forward_written(b, T * k, E)
     ref = {n: b[n].clone() for n in ("out", "topk_ids", "topk_weights", "y")}
 
     graph = torch.cuda.CUDAGraph()

@@ -5,11 +5,14 @@ expert, every token on the same experts, exact ties)."""
 import numpy as np
 import pytest
 import torch
+from hypothesis import HealthCheck, Phase, given, settings
+from hypothesis import strategies as hst
 
 import oracle
 from group_limited_routing_router_amd.inputs import CONFIGS, MoEConfig, bits, make_inputs
 
-from _parity import OUT_TOL, compare_routing, out_error
+from _parity import (OUT_TOL, assert_forward_written, compare_routing, out_error,
+                     sentinel_buffers)
 
 pytestmark = pytest.mark.gpu
 
@@ -27,8 +30,10 @@ def _to_gpu(d):
 
 
 def _run_steps(moe, cfg, g, bias=True):
+    """The four steps into sentinel-filled buffers (NaN, -1, 0xFF): every
+    output element must be written."""
     p = moe.MoEProblem.from_config(cfg)
-    b = moe.alloc_buffers(p)
+    b = sentinel_buffers(moe, p)
     moe.moe_route(p, g["x"], g["w_router"], g["bias"] if bias else None, b["topk_ids"],
                   b["topk_weights"])
     moe.moe_permute(p, b["topk_ids"], b["expert_offsets"], b["sorted_pairs"], b["pair_rows"],
@@ -37,6 +42,8 @@ def _run_steps(moe, cfg, g, bias=True):
                        g["w_down"], b["y"], b["ws"])
     moe.moe_combine(p, b["y"], b["pair_rows"], b["topk_weights"], b["out"])
     torch.cuda.synchronize()
+    assert_forward_written(b, cfg.T * cfg.k, cfg.E)
+    assert int(b["sorted_pairs"].min()) >= 0 and int(b["pair_rows"].min()) >= 0
     return p, {k: v.cpu().numpy() if v.dtype != torch.bfloat16 else v.cpu() for k, v in b.items()}
 
 
@@ -159,7 +166,7 @@ def test_forward_matches_steps_bf16_and_determinism(moe):
     p, r = _run_steps(moe, cfg, g)
     outs = []
     for dtype in (torch.float32, torch.float32, torch.bfloat16):
-        b = moe.alloc_buffers(p, out_dtype=dtype)
+        b = sentinel_buffers(moe, p, out_dtype=dtype)
         moe.moe_forward(p, g["x"], g["w_router"], g["bias"], g["w_gate"], g["w_up"], g["w_down"],
                         b["out"], b["topk_ids"], b["topk_weights"], b["y"], b["ws"])
         torch.cuda.synchronize()
@@ -172,7 +179,7 @@ def test_forward_matches_steps_bf16_and_determinism(moe):
     # bf16 output is the round-to-nearest-even cast of the fp32 output
     assert torch.equal(outs[2].view(torch.int16), outs[0].to(torch.bfloat16).view(torch.int16))
     # forward without routing outputs (kept in the workspace) gives the same out
-    b = moe.alloc_buffers(p)
+    b = sentinel_buffers(moe, p)
     moe.moe_forward(p, g["x"], g["w_router"], g["bias"], g["w_gate"], g["w_up"], g["w_down"],
                     b["out"], None, None, b["y"], b["ws"])
     torch.cuda.synchronize()
@@ -185,3 +192,77 @@ def test_zero_tokens_gpu(moe):
     b = moe.alloc_buffers(p)
     moe.moe_forward(p, None, None, None, None, None, None, b["out"], None, None, None, None)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [700, 1500])
+def test_permute_drops_out_of_range_ids(moe, T):
+    """moe_permute's documented handling of ids outside [0, E): the pair is
+    dropped (pair_rows = -1), expert_offsets count only the kept pairs, the
+    kept pairs keep the stable order, and sorted positions past the kept
+    pairs are not written.  moe_combine then counts a dropped pair as 0.
+    (The oracle rejects such ids -- they are not routing results -- so the
+    expected permutation here is numpy's stable sort of the kept pairs.)
+    700 tokens use the one-workgroup permutation, 1500 the three launches."""
+    cfg = MoEConfig("drop", T=T, H=256, I=128, E=16, G=4, TG=2, k=4, scale=2.5)
+    E, k = cfg.E, cfg.k
+    print(f"[case] permute drop T={T}", flush=True)
+    rng = np.random.default_rng(T)
+    ids = rng.integers(0, E, size=(T, k)).astype(np.int32)
+    bad = rng.random((T, k)) < 0.1
+    ids[bad] = rng.choice(np.array([-1, -100, E, E + 5, 2 ** 31 - 1], np.int32), int(bad.sum()))
+    p = moe.MoEProblem.from_config(cfg)
+    b = sentinel_buffers(moe, p)
+    for key in ("sorted_pairs", "pair_rows", "expert_offsets"):
+        b[key].fill_(-7)
+    gi = torch.from_numpy(ids).cuda()
+    moe.moe_permute(p, gi, b["expert_offsets"], b["sorted_pairs"], b["pair_rows"], b["ws"])
+    torch.cuda.synchronize()
+    flat = ids.ravel()
+    keep = (flat >= 0) & (flat < E)
+    kept = np.nonzero(keep)[0]
+    order = kept[np.argsort(flat[kept], kind="stable")]
+    off = np.concatenate([[0], np.cumsum(np.bincount(flat[kept], minlength=E))]).astype(np.int32)
+    rows = np.full(T * k, -1, np.int32)
+    rows[order] = np.arange(order.size, dtype=np.int32)
+    np.testing.assert_array_equal(b["expert_offsets"].cpu().numpy(), off)
+    sp = b["sorted_pairs"].cpu().numpy()
+    np.testing.assert_array_equal(sp[:order.size], order)
+    assert np.all(sp[order.size:] == -7), "sorted positions past the kept pairs were written"
+    np.testing.assert_array_equal(b["pair_rows"].cpu().numpy(), rows)
+    # combine: dropped pairs contribute 0
+    y = torch.randn((T * k, cfg.H), dtype=torch.float32, device="cuda")
+    w = torch.rand((T, k), dtype=torch.float32, device="cuda")
+    moe.moe_combine(p, y, b["pair_rows"], w, b["out"])
+    torch.cuda.synchronize()
+    yp = np.zeros((T * k, cfg.H), np.float32)
+    yp[kept] = y.cpu().numpy()[rows[kept]]
+    want = oracle.combine(yp, w.cpu().numpy(), cfg.scale)
+    err, _ = out_error(b["out"].cpu().numpy(), want)
+    assert err <= 1e-5
+
+
+@hst.composite
+def _problems(draw):
+    G = draw(hst.sampled_from([1, 2, 3, 4, 8]))
+    per = draw(hst.sampled_from([1, 2, 4, 8, 16, 32]))
+    TG = draw(hst.integers(1, G))
+    k = draw(hst.integers(1, min(16, TG * per)))
+    H = draw(hst.sampled_from([128, 256, 384, 512]))
+    I = draw(hst.sampled_from([64, 128, 192, 256, 384]))
+    T = draw(hst.integers(1, 640))
+    seed = draw(hst.integers(0, 2 ** 20))
+    return (T, H, I, G * per, G, TG, k, seed)
+
+
+@settings(max_examples=40, deadline=None, derandomize=True, database=None,
+          phases=(Phase.explicit, Phase.generate), print_blob=True,
+          suppress_health_check=[HealthCheck.too_slow, HealthCheck.data_too_large])
+@given(prob=_problems())
+def test_property_random_shapes(moe, prob):
+    """Hypothesis over small (T, H, I, E, G, TG, k): every step against the
+    oracle (routing, exact permutation, y, combine, end to end) with sentinel
+    outputs.  Examples are derived deterministically and not shrunk: the run
+    stops at the first failing example, which it prints."""
+    T, H, I, E, G, TG, k, seed = prob
+    cfg = MoEConfig("prop", T=T, H=H, I=I, E=E, G=G, TG=TG, k=k, scale=2.5)
+    _check_all(moe, cfg, make_inputs(cfg, seed=seed), f"property seed={seed}")
