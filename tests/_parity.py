@@ -37,6 +37,35 @@ def boundary_gaps(scores, gscores, E, G, TG, k):
     return g_gap, e_gap
 
 
+def valid_near_tie(gi, s, gs, E, G, TG, k):
+    """For a token with a near tie (gap < GAP) at a selection boundary: is the
+    GPU's id set gi one the method gives under some resolution of the ties?
+    Every group whose oracle score is more than GAP above the TG-th best is
+    kept; the groups within GAP of it fill the remaining places in any
+    combination; for each such kept set the top-k experts of its groups
+    (oracle fp32 scores) must equal gi, or gi must lie in those groups with a
+    score sum no lower than the top-k's minus k * GAP (a near tie at the
+    expert boundary)."""
+    from itertools import combinations
+
+    gsz = E // G
+    gs = gs.astype(np.float64)
+    s = s.astype(np.float64)
+    thr = np.sort(gs)[::-1][TG - 1]
+    sure = [g for g in range(G) if gs[g] > thr + GAP]
+    tied = [g for g in range(G) if abs(gs[g] - thr) <= GAP and g not in sure]
+    want = set(int(e) for e in gi)
+    for combo in combinations(tied, TG - len(sure)):
+        kept = sorted(sure + list(combo))
+        cand = np.concatenate([np.arange(g * gsz, (g + 1) * gsz) for g in kept])
+        top = cand[np.lexsort((cand, -s[cand]))][:k]
+        if want == set(top.tolist()):
+            return True
+        if want <= set(cand.tolist()) and s[list(want)].sum() >= s[top].sum() - k * GAP:
+            return True
+    return False
+
+
 def compare_routing(gpu_ids, gpu_w, ora_ids, ora_w, scores, gscores, E, G, TG, k):
     """Asserts the routing contract; returns (exempt mask, stats dict)."""
     T = gpu_ids.shape[0]
@@ -52,9 +81,8 @@ def compare_routing(gpu_ids, gpu_w, ora_ids, ora_w, scores, gscores, E, G, TG, k
         assert len({int(e) // gsz for e in gi}) <= TG, f"token {t}: more than TG groups"
         assert abs(float(gpu_w[t].astype(np.float64).sum()) - 1.0) <= 1e-5
         if exempt[t]:
-            sg = float(scores[t, gi].astype(np.float64).sum())
-            so = float(scores[t, oi].astype(np.float64).sum())
-            assert sg >= so - 1e-5 * k, f"token {t}: exempt choice worse than oracle"
+            assert valid_near_tie(gi, scores[t], gscores[t], E, G, TG, k), \
+                f"token {t}: near-tie choice {gi} is not one the method allows (oracle {oi})"
             continue
         if set(gi.tolist()) != set(oi.tolist()):
             bad.append(t)
@@ -72,6 +100,17 @@ def compare_routing(gpu_ids, gpu_w, ora_ids, ora_w, scores, gscores, E, G, TG, k
             assert abs(wg[e] - w) <= W_TOL, f"token {t}: weight of {e}: {wg[e]} vs {w}"
     assert not bad, f"routing differs on non-exempt tokens {bad[:10]} (of {len(bad)})"
     return exempt, dict(tokens=T, exempt=int(exempt.sum()))
+
+
+def h_error(gpu_h, ref_h):
+    """The SwiGLU product h is rounded to bf16 on both sides from fp32 values
+    that differ by the accumulation order, so an element may land one bf16
+    step (at most 2^-7 of its magnitude) away, plus fp32-level noise.  Returns
+    max |gpu - ref| / (2^-7 |ref| + 1e-3 RMS(ref)); <= 1 passes."""
+    ref = np.asarray(ref_h, np.float64)
+    err = np.abs(np.asarray(gpu_h, np.float64) - ref)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    return float((err / (2.0 ** -7 * np.abs(ref) + 1e-3 * rms + 1e-30)).max())
 
 
 def out_error(gpu_out, ref_out):
