@@ -7,6 +7,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
 #include <string>
 
 #include "moe.h"
@@ -124,6 +125,36 @@ moe_status hip_status(hipError_t e, const char* what) {
 template <typename T>
 T* at(void* ws, size_t off) {
     return reinterpret_cast<T*>(static_cast<char*>(ws) + off);
+}
+
+// The workspace of moe_forward_noalloc: a fixed array in device memory, one
+// copy per GPU that holds it until the process ends.  Host code never uses
+// its name as an address: the device address of each GPU's copy comes from
+// hipGetSymbolAddress (looked up on the first call on that GPU).
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current GPU's scratch array (looked up once per GPU).
+moe_status device_scratch(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "device %d beyond the %d the library tracks", dev,
+                    kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+        if (!ptr) return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch) gave NULL");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
 }
 
 }  // namespace
@@ -401,6 +432,41 @@ MOE_EXPORT moe_status moe_forward(const moe_problem* p, const moe_bf16* x,
     if (e != hipSuccess) return hip_status(e, "expert ffn launch");
     e = moe::launch_combine(q, y, rows, wts, out, out_dtype == MOE_DTYPE_BF16, stream);
     return hip_status(e, "combine launch");
+}
+
+MOE_EXPORT moe_status moe_forward_noalloc(const moe_problem* p, const moe_bf16* x,
+                                          const moe_bf16* w_router, const float* bias,
+                                          const moe_bf16* w_gate, const moe_bf16* w_up,
+                                          const moe_bf16* w_down, void* out, moe_dtype out_dtype,
+                                          int32_t* topk_ids, float* topk_weights, float* y,
+                                          hipStream_t stream) {
+    MOE_TRY(check_problem(p));
+    if (out_dtype != MOE_DTYPE_F32 && out_dtype != MOE_DTYPE_BF16)
+        return fail(MOE_ERR_INVALID_ARG, "out_dtype=%d is not MOE_DTYPE_F32/BF16", (int)out_dtype);
+    if (p->T == 0) return ok();
+    MOE_TRY(check_ptr(x, "x"));
+    MOE_TRY(check_ptr(w_router, "w_router"));
+    MOE_TRY(check_ptr(bias, "bias", true));
+    MOE_TRY(check_ptr(w_gate, "w_gate"));
+    MOE_TRY(check_ptr(w_up, "w_up"));
+    MOE_TRY(check_ptr(w_down, "w_down"));
+    MOE_TRY(check_ptr(out, "out"));
+    MOE_TRY(check_ptr(topk_ids, "topk_ids", true));
+    MOE_TRY(check_ptr(topk_weights, "topk_weights", true));
+    MOE_TRY(check_ptr(y, "y"));
+    const size_t need = layout_of(*p).total;
+    if (need > static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "the problem needs %zu bytes of scratch; the static scratch holds %zu "
+                    "(call moe_forward with a workspace)",
+                    need, static_cast<size_t>(MOE_NOALLOC_SCRATCH_BYTES));
+    void* ws = nullptr;
+    MOE_TRY(device_scratch(&ws));
+    // the same kernels and workspace layout as moe_forward; nothing in the
+    // workspace has to start at zero (every scratch value is written before
+    // it is read), so the previous call's contents need no clearing
+    return moe_forward(p, x, w_router, bias, w_gate, w_up, w_down, out, out_dtype, topk_ids,
+                       topk_weights, y, ws, need, stream);
 }
 
 MOE_EXPORT const char* moe_status_string(moe_status s) {

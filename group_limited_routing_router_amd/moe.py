@@ -26,6 +26,7 @@ _lib = None
 MOE_OK = 0
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MOE_NOALLOC_SCRATCH_BYTES of moe.h
 
 _STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARG", 2: "MOE_ERR_UNSUPPORTED",
            3: "MOE_ERR_WORKSPACE", 4: "MOE_ERR_HIP"}
@@ -51,7 +52,7 @@ class MoEProblem(ctypes.Structure):
 EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
            "moe_expert_gate_up", "moe_expert_down", "moe_combine", "moe_combine_residual",
            "moe_dense_mlp", "moe_expert_ffn_fp8", "moe_forward", "moe_forward_fp8",
-           "moe_status_string", "moe_last_error",
+           "moe_forward_noalloc", "moe_status_string", "moe_last_error",
            # measurement kernels (include/moe_peak.h)
            "moe_peak_stream_read", "moe_peak_mfma_bf16", "moe_peak_mfma_bf16_flops")
 
@@ -117,6 +118,8 @@ def load_library():
         lib.moe_forward.argtypes = [prob, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, P,
                                     ctypes.c_size_t, P]
         lib.moe_forward.restype = st
+        lib.moe_forward_noalloc.argtypes = [prob, P, P, P, P, P, P, P, ctypes.c_int, P, P, P, P]
+        lib.moe_forward_noalloc.restype = st
         lib.moe_peak_stream_read.argtypes = [P, ctypes.c_size_t, ctypes.c_int, P, ctypes.c_int, P]
         lib.moe_peak_stream_read.restype = st
         lib.moe_peak_mfma_bf16.argtypes = [ctypes.c_int64, P, ctypes.c_int, P]
@@ -240,6 +243,14 @@ def moe_forward(p, x, w_router, bias, w_gate, w_up, w_down, out, topk_ids, topk_
                                        _p(w_up), _p(w_down), _p(out), _dtype_code(out),
                                        _p(topk_ids), _p(topk_weights), _p(y), _p(ws), nbytes,
                                        _stream(stream)))
+
+
+def moe_forward_noalloc(p, x, w_router, bias, w_gate, w_up, w_down, out, topk_ids, topk_weights,
+                        y, stream=None):
+    _check(load_library().moe_forward_noalloc(ctypes.byref(p), _p(x), _p(w_router), _p(bias),
+                                               _p(w_gate), _p(w_up), _p(w_down), _p(out),
+                                               _dtype_code(out), _p(topk_ids), _p(topk_weights),
+                                               _p(y), _stream(stream)))
 
 
 def moe_peak_stream_read(buf, sink, workgroups, nontemporal=False, stream=None):

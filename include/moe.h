@@ -231,6 +231,26 @@ moe_status moe_forward(const moe_problem* p, const moe_bf16* x, const moe_bf16* 
                        float* topk_weights, float* y, void* ws, size_t ws_bytes,
                        hipStream_t stream);
 
+/* moe_forward for callers that cannot allocate (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): no workspace
+ * argument.  The workspace is a fixed array of MOE_NOALLOC_SCRATCH_BYTES in
+ * device memory inside the library, one copy per GPU, held until the process
+ * ends; the call allocates and frees nothing.  Problems that need more
+ * (moe_workspace_bytes(p) > MOE_NOALLOC_SCRATCH_BYTES; at Beam's sizes about
+ * 1600 tokens) return MOE_ERR_UNSUPPORTED before anything is enqueued.
+ * Arguments, outputs and results are those of moe_forward, bit for bit.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (two streams, two host threads) race and give undefined results; calls
+ * ordered on one stream are safe.  The first call on a GPU looks the array up
+ * (hipGetSymbolAddress); make it outside graph capture. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+moe_status moe_forward_noalloc(const moe_problem* p, const moe_bf16* x, const moe_bf16* w_router,
+                               const float* bias, const moe_bf16* w_gate, const moe_bf16* w_up,
+                               const moe_bf16* w_down, void* out, moe_dtype out_dtype,
+                               int32_t* topk_ids, float* topk_weights, float* y,
+                               hipStream_t stream);
+
 /* Static text for a status code. */
 const char* moe_status_string(moe_status s);
 

@@ -197,3 +197,25 @@ def test_measurement_kernels_reject_bad_arguments(lib):
     assert cdll.moe_peak_mfma_bf16(i64(10), None, 16, None) == 1
     # FLOPs of one call: waves x steps x 8 chains x 2*32*32*16
     assert lib.load_library().moe_peak_mfma_bf16_flops(i64(100), 3) == 3 * 4 * 100 * 8 * 32768
+
+
+def test_noalloc_forward_host_checks(lib):
+    """moe_forward_noalloc: T = 0 is a no-op; a problem whose workspace would
+    not fit the static scratch is refused before anything is enqueued."""
+    cdll = lib.load_library()
+    keep, good = _aligned()
+    guard = np.full(16, 3, np.int32)
+    assert cdll.moe_forward_noalloc(ctypes.byref(_beam(0)), None, None, None, None, None, None,
+                                    None, 0, None, None, None, None) == 0
+    big = _beam(4096)
+    assert lib.moe_workspace_bytes(big) > lib.NOALLOC_SCRATCH_BYTES
+    assert cdll.moe_forward_noalloc(ctypes.byref(big), good, good, None, good, good, good,
+                                    guard.ctypes.data, 0, None, None, good, None) == 2
+    assert b"static scratch" in cdll.moe_last_error()
+    assert cdll.moe_forward_noalloc(ctypes.byref(_beam()), good, good, None, good, good, good,
+                                    guard.ctypes.data, 0, None, None, None, None) == 1
+    assert np.all(guard == 3)
+    # the header's limit and the binding's copy of it agree
+    text = open(HEADER).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+    assert lib.NOALLOC_SCRATCH_BYTES == 64 << 20
