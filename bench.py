@@ -293,7 +293,7 @@ def achievable_peaks(repeats=5):
 
     reads = {}
     for nt in (False, True):
-        for wg in (1024, 2048, 4096, 8192):
+        for wg in (2048, 8192, 16384, 32768):
             ms = best_ms(lambda: moe.moe_peak_stream_read(buf, sink, wg, nontemporal=nt))
             reads[f"{'nt' if nt else 'cached'}_wg{wg}"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
     del buf, sink
@@ -573,6 +573,8 @@ def summarize_trace(path, skip):
              "    avg_us    med_us    min_us    max_us"]
     for k, v in sorted(by.items(), key=lambda kv: STEPS.index(step_of(kv[0]).replace("fp8_", ""))
                        if step_of(kv[0]).replace("fp8_", "") in STEPS else 99):
+        if step_of(k) == "other":  # torch's own kernels (input draws, copies)
+            continue
         d = [x[0] / 1e3 for x in v[skip:]] or [x[0] / 1e3 for x in v]
         lines.append(f"  {step_of(k):<18} {k:<48} {v[0][1]:>9} {len(d):>6} {sum(d) / len(d):>9.1f} "
                      f"{statistics.median(d):>9.1f} {min(d):>9.1f} {max(d):>9.1f}")
