@@ -548,21 +548,38 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
         constexpr int NV = decltype(nv_tag)::value;
         constexpr int NA = NV > 0 ? NV : 1;
         constexpr int MF = NV * NFB;  // MFMAs per substep
-        // B fragments are held as read: bf16, or 8 E4M3 codes widened to bf16
+        // B fragments are held as read: bf16, or E4M3 codes widened to bf16
         // right before the MFMAs that use them (converting at the read would
-        // wait out the LDS latency there)
-        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-        typedef typename std::conditional<FP8, u32x2, bf16x8>::type BFrag;
+        // wait out the LDS latency there).
+        //
+        // FP8: substeps go in pairs (2p, 2p + 1), which cover codes
+        // [32 p, 32 p + 32) of the activation stage's half of the weight stage.
+        // In the even substep every lane reads one whole 16-byte chunk of codes
+        // -- lanes below 32 chunk 2p, the others chunk 2p + 1 -- and the pair's
+        // two MFMAs take its first and its second 8 bytes.  The MFMA's k lanes
+        // then stand for physical k = 16 (2p + half) + 8 j + (0..7) in substep
+        // 2p + j, and the A fragments follow the same mapping (activation
+        // chunk 4p + 2 half + j).  Every product is the same; only the order of
+        // the fp32 sum changes.  The reads are whole chunks, 16 lanes to 16
+        // rows of one chunk, so the swizzle keeps them free of bank conflicts
+        // (8-byte half-chunk reads met 2-way conflicts on about 30% of LDS
+        // accesses).  The second 8 bytes are widened together with the first
+        // (bh), so the raw codes are dead after the even substep and the next
+        // pair's chunks load during the odd one.
+        typedef typename std::conditional<FP8, u32x4, bf16x8>::type BFrag;
         struct Frags {
             bf16x8 a[NA];
             BFrag b[NFB];
         };
-        // piece q of substep ks's fragments: A blocks first, then B blocks
-        // (FP8: from half hb of the weight stage)
+        bf16x8 bh[FP8 ? NFB : 1];  // FP8: codes 8..15 of the pair's chunks, widened
+        // fragment pieces of substep ks: A blocks first, then B blocks (none
+        // in an odd FP8 substep: the pair's chunks are already held)
+        auto pieces = [](int ks) { return NV > 0 ? NV + ((FP8 && (ks & 1)) ? 0 : NFB) : 0; };
+        // piece q of substep ks's fragments (FP8: from half hb of the weight stage)
         auto load_piece = [&](Frags& f, int ab, int bb, int ks, int hb, auto qc) {
             constexpr int q = decltype(qc)::value;
-            const int c = ks * 2 + half;
             if constexpr (q < NV) {
+                const int c = FP8 ? 4 * (ks >> 1) + 2 * half + (ks & 1) : ks * 2 + half;
                 const unsigned char* sa = s_arena + (a_buf(ab) - arena);
                 f.a[q] = *reinterpret_cast<const bf16x8*>(sa + frag_off((wm + WAVES_M * q) * 32 + r32, c));
             } else if constexpr (NV > 0) {
@@ -571,31 +588,38 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
                 const unsigned char* sb = s_arena + (b_buf(bb) - arena);
                 const int br = g * BN_OUT + wn * WN_OUT + n * 32 + r32;
                 if constexpr (FP8) {
-                    // 8 codes: 8-byte half `half` of 16-byte chunk 4 hb + ks
-                    f.b[gn] = *reinterpret_cast<const u32x2*>(sb + frag_off(br, hb * 4 + ks) + (half << 3));
+                    // 16 codes: chunk 4 hb + ks + half (ks even)
+                    f.b[gn] = *reinterpret_cast<const u32x4*>(sb + frag_off(br, hb * 4 + ks + half));
                 } else {
-                    f.b[gn] = *reinterpret_cast<const bf16x8*>(sb + frag_off(br, c));
+                    f.b[gn] = *reinterpret_cast<const bf16x8*>(sb + frag_off(br, ks * 2 + half));
                 }
             }
         };
-        constexpr int NP = NV > 0 ? NV + NFB : 0;  // fragment pieces per substep
+        constexpr int NP = NV > 0 ? NV + NFB : 0;  // most fragment pieces of a substep
         auto load_frags = [&](Frags& f, int ab, int bb, int ks, int hb) {
-            static_for<0, NP>([&](auto qc) { load_piece(f, ab, bb, ks, hb, qc); });
+            static_for<0, NP>([&](auto qc) {
+                if (decltype(qc)::value < pieces(ks)) load_piece(f, ab, bb, ks, hb, qc);
+            });
         };
-        // MFMA i = (g * NB + n) * NV + m of a substep; bop holds B fragment gn
-        // in bf16 (FIRST: MFMA i is the first of a run on it, so it is
-        // widened here)
-        auto mfma_one = [&](const Frags& f, auto ic, bf16x8& bop, bool first) {
+        // MFMA i = (g * NB + n) * NV + m of substep ks; bop holds B fragment
+        // gn in bf16 (FIRST: MFMA i is the first of a run on it, so it is
+        // widened, or for an odd FP8 substep taken from bh, here)
+        auto mfma_one = [&](const Frags& f, auto ic, auto ks_c, bf16x8& bop, bool first) {
             constexpr int i = decltype(ic)::value;
+            constexpr int KS = decltype(ks_c)::value;
             constexpr int m = i % (NV > 0 ? NV : 1);
             constexpr int gn = i / (NV > 0 ? NV : 1);
             constexpr int g = gn / NB, n = gn % NB;
             if constexpr (NV > 0) {
                 if (m == 0 || first) {  // compile-time at every call site
-                    if constexpr (FP8)
+                    if constexpr (FP8 && (KS & 1)) {
+                        bop = bh[gn];
+                    } else if constexpr (FP8) {
                         bop = e4m3x8_to_bf16x8(f.b[gn][0], f.b[gn][1]);
-                    else
+                        bh[gn] = e4m3x8_to_bf16x8(f.b[gn][2], f.b[gn][3]);
+                    } else {
                         bop = f.b[gn];
+                    }
                 }
                 acc[g][m][n] = mfma32(f.a[m], bop, acc[g][m][n]);
             }
@@ -641,13 +665,14 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
             // MFMAs [LO, HI) of substep SUB with its stage loads spread over them
             // (none for a negative SUB) and, for KN >= 0, the fragments of
             // substep KN read into FN piece by piece between them
-            auto substep = [&](const Frags& f, auto sc, auto lo_c, auto hi_c, Frags& fn, auto kn_c) {
+            // (KS: the substep whose MFMAs these are, 0..3)
+            auto substep = [&](const Frags& f, auto sc, auto ks_c, auto lo_c, auto hi_c, Frags& fn, auto kn_c) {
                 constexpr int sub = decltype(sc)::value;
                 constexpr int LO = decltype(lo_c)::value, HI = decltype(hi_c)::value;
                 constexpr int KN = decltype(kn_c)::value;
                 constexpr int NM = HI - LO;
                 constexpr int NL = sub >= 0 ? LPS : 0;
-                constexpr int NPC = KN >= 0 ? NP : 0;
+                constexpr int NPC = KN >= 0 ? (NV > 0 ? NV + ((FP8 && (KN & 1)) ? 0 : NFB) : 0) : 0;
                 constexpr int IT = NM > NL ? (NM > 0 ? NM : 1) : (NL > 0 ? NL : 1);
                 bf16x8 bop;
                 static_for<0, IT>([&](auto ic) {
@@ -656,7 +681,7 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
                         constexpr int q = decltype(qc)::value;
                         if constexpr (q * IT / (NPC > 0 ? NPC : 1) == i) load_piece(fn, abuf, bbuf, KN, HB, qc);
                     });
-                    if constexpr (i < NM) mfma_one(f, std::integral_constant<int, LO + i>{}, bop, i == 0);
+                    if constexpr (i < NM) mfma_one(f, std::integral_constant<int, LO + i>{}, ks_c, bop, i == 0);
                     constexpr int step = NM >= NL ? (NL > 0 ? NM / NL : 1) : 1;
                     if constexpr (NL > 0 && i % step == step - 1 && i / step < NL) {
                         constexpr int j = sub * LPS + i / step;
@@ -672,17 +697,21 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_dma_kernel(FfnArgs a) {
             using CM = std::integral_constant<int, MF>;
             using CH = std::integral_constant<int, MF * 7 / 8>;
             using KNone = std::integral_constant<int, -1>;
-            substep(f0, std::integral_constant<int, 0>{}, C0{}, CM{}, f1, std::integral_constant<int, 1>{});
-            substep(f1, std::integral_constant<int, 1>{}, C0{}, CM{}, f0, std::integral_constant<int, 2>{});
-            substep(f0, std::integral_constant<int, 2>{}, C0{}, CM{}, f1, std::integral_constant<int, 3>{});
-            substep(f1, std::integral_constant<int, 3>{}, C0{}, CH{}, f0, KNone{});
+            using K0 = std::integral_constant<int, 0>;
+            using K1 = std::integral_constant<int, 1>;
+            using K2 = std::integral_constant<int, 2>;
+            using K3 = std::integral_constant<int, 3>;
+            substep(f0, K0{}, K0{}, C0{}, CM{}, f1, K1{});
+            substep(f1, K1{}, K1{}, C0{}, CM{}, f0, K2{});
+            substep(f0, K2{}, K2{}, C0{}, CM{}, f1, K3{});
+            substep(f1, K3{}, K3{}, C0{}, CH{}, f0, KNone{});
             wait_vmcnt<DMA_B>();
             __syncthreads();
             abuf = anext;
             if constexpr (HB == SB - 1) bbuf = bbuf == 2 ? 0 : bbuf + 1;
             load_frags(f0, abuf, bbuf, 0, (HB + 1) % SB);  // after the last stage: read, never used
             __builtin_amdgcn_sched_barrier(0);
-            substep(f1, std::integral_constant<int, -1>{}, CH{}, CM{}, f0, KNone{});
+            substep(f1, std::integral_constant<int, -1>{}, K3{}, CH{}, CM{}, f0, KNone{});
         });
         wait_vmcnt<0>();
         __syncthreads();
