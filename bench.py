@@ -28,6 +28,7 @@ Other modes (one JSON line or a text table each):
   --gemm-study         the prefill expert GEMMs at fixed rows per expert
   --summarize-trace D  per-kernel durations from a rocprofv3 kernel trace
   --summarize-pmc D1 D2  HBM bytes per launch from FETCH_SIZE / WRITE_SIZE runs
+  --summarize-counters D per-kernel averages of any counter run
 """
 from __future__ import annotations
 
@@ -656,6 +657,42 @@ def summarize_pmc(fetch_path, write_path, skip, workload=None, update=False):
         log(f"[bench] traffic of {workload} stored under kernel sources {sha}")
 
 
+def summarize_counters(path, skip):
+    """Per kernel of the block: every counter of a rocprofv3 --pmc run,
+    summed over the dispatch's rows and averaged over the launches after the
+    first `skip`; with SQ_LDS_BANK_CONFLICT and SQ_LDS_IDX_ACTIVE the share
+    of LDS cycles lost to bank conflicts, with SQ_VALU_MFMA_BUSY_CYCLES and
+    GRBM_GUI_ACTIVE the MFMA busy fraction per SIMD (1024 SIMDs, 8 XCDs)."""
+    rows = _csv_files(path, "counter_collection.csv")
+    per, names = {}, {}
+    for r in rows:
+        k = short_kernel_name(r["Kernel_Name"])
+        if step_of(k) == "other":
+            continue
+        d = int(r["Dispatch_Id"])
+        names[d] = k
+        per.setdefault(d, {}).setdefault(r["Counter_Name"], 0.0)
+        per[d][r["Counter_Name"]] += float(r["Counter_Value"])
+    by = {}
+    for d in sorted(per):
+        by.setdefault(names[d], []).append(per[d])
+    lines = [f"# skipped: the first {skip} launches of each kernel"]
+    for k, lst in by.items():
+        lst = lst[skip:] or lst
+        avg = {c: sum(x.get(c, 0.0) for x in lst) / len(lst) for c in lst[0]}
+        derived = []
+        if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
+            derived.append("lds_bank_conflict_share=%.3f" % (avg["SQ_LDS_BANK_CONFLICT"] /
+                                                            avg["SQ_LDS_IDX_ACTIVE"]))
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in avg and avg.get("GRBM_GUI_ACTIVE"):
+            derived.append("mfma_busy=%.3f" % (avg["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 /
+                                               (avg["GRBM_GUI_ACTIVE"] / 8)))
+        lines.append(f"  {step_of(k):<18} {k:<48} launches={len(lst)} " + " ".join(
+            f"{c}={v:.4g}" for c, v in sorted(avg.items())) + ("  " + " ".join(derived)
+                                                              if derived else ""))
+    print("\n".join(lines))
+
+
 def kernels_only(args, weights):
     """The timed workload's steps as separate calls only (warmup + steps
     launches of each kernel, nothing else on the GPU), optionally with the
@@ -727,6 +764,8 @@ def main():
                     help="print per-kernel durations of a rocprofv3 kernel trace (no GPU)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print HBM bytes per launch from two rocprofv3 --pmc runs (no GPU)")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print per-kernel averages of any rocprofv3 --pmc run (no GPU)")
     ap.add_argument("--skip", type=int, default=0,
                     help="with --summarize-*: leave out the first N launches of each kernel")
     ap.add_argument("--update-traffic", action="store_true",
@@ -740,6 +779,9 @@ def main():
         sys.exit(2)
     if args.summarize_trace:
         summarize_trace(args.summarize_trace, args.skip)
+        return
+    if args.summarize_counters:
+        summarize_counters(args.summarize_counters, args.skip)
         return
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc, args.skip, args.workload, args.update_traffic)
