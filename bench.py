@@ -10,8 +10,9 @@ tokens, hidden 5120, 256 experts in 8 groups (4 kept), k=8, intermediate
 2560, bf16 weights and activations with fp32 accumulation.  The decode batch
 (T=128, the HBM half of the headline metric), the skewed (T=4096) and long
 (T=65536) workloads are timed the same way and reported as secondary objects,
-with the FP8-weight layer and the dense MLP.  Inputs are seeded synthetic
-Gaussians (no trained weights exist here).
+with the FP8-weight layer and the dense MLP; the prefill and decode forward
+is also timed as a replayed HIP graph (`graph_replay`).  Inputs are seeded
+synthetic Gaussians (no trained weights exist here).
 
 Prints one JSON line.  `value` is tokens/s of the timed workload (mean wall
 time of exactly --steps calls between two device synchronisations; the
@@ -175,6 +176,30 @@ def run_workload(name, steps, warmup, weights, forward=True, kernels=True):
         hot = torch.nonzero(d["bias"] > 0).flatten()
         res["hot_share"] = round(float(torch.isin(ids.flatten(), hot.to(ids.dtype)).float().mean()), 4)
     return res
+
+
+def graph_replay_ms(res, steps, warmup):
+    """The same moe_forward captured once into a HIP graph (the library's
+    calls are capture-safe) and replayed: ms per replay, events on the
+    current stream.  Shows what the per-call launch overhead costs."""
+    import torch
+
+    from group_limited_routing_router_amd import moe
+
+    cfg, d, b = res["cfg"], res["inputs"], res["buffers"]
+    p = moe.MoEProblem.from_config(cfg)
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            moe.moe_forward(p, d["x"], d["w_router"], d["bias"], d["w_gate"], d["w_up"],
+                            d["w_down"], b["out"], b["topk_ids"], b["topk_weights"], b["y"], b["ws"])
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ms, step_ms = timed_steps(g.replay, steps, warmup)
+    del g
+    return {"ms_per_step": round(ms, 4), **step_stats(step_ms)}
 
 
 def workload_summary(res, peaks=None):
@@ -847,6 +872,7 @@ def main():
         # the timed step: a separate entry point after the block)
         "combine_residual": roofline_for(main_res, "combine_residual"),
     }
+    out["graph_replay"] = graph_replay_ms(main_res, args.steps, args.warmup)
     if peaks:
         out["achievable_hbm_gbs"] = peaks["achievable_hbm_gbs"]
         out["achievable_mfma_tflops"] = peaks["achievable_mfma_tflops"]
@@ -859,6 +885,8 @@ def main():
                 continue
             r = run_workload(name, args.steps, args.warmup, weights)
             out[name] = workload_summary(r, peaks)
+            if name == "decode":
+                out[name]["graph_replay"] = graph_replay_ms(r, args.steps, args.warmup)
             log("[bench] %s T=%d: %.3f ms/step, %.1f%% of bf16 MFMA peak, %.1f%% of HBM peak" % (
                 name, r["cfg"].T, r["ms"], 100 * out[name]["mfma_frac"],
                 100 * out[name]["hbm_frac"]))
