@@ -70,6 +70,8 @@ struct FfnArgs {
     const float* s0;         // FP8 weights only: per-channel scales of b0 [E,N]
     const float* s1;         // and of b1
     bool stream_out = false; // large-tile down: y stores stream past the caches
+    bool stream_w = false;   // small tiles: every weight is read once (about one row
+                             // tile per expert), so it streams past the caches
 };
 
 // Map this workgroup to a tile (expert e, column tile nt, row range
@@ -176,7 +178,8 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16x8(uint32_t lo, uint32_t hi) {
 // as each MFMA operand is read, and the channel scale multiplies the fp32
 // accumulator in the epilogue.  SK is the K extent of an LDS stage: 128 for
 // FP8 weights, so that every weight row of a stage is one whole 128-byte line.
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP, bool FP8 = false, int SK = 64>
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP, bool FP8 = false, int SK = 64,
+          bool NTW = false>
 __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     static_assert(WAVES_M * WAVES_N == kWaves, "4 waves");
     static_assert(SK == 64 || SK == 128, "stage depth");
@@ -254,10 +257,12 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
             if (A_CHUNKS % kThreads == 0 || tid + i * kThreads < A_CHUNKS) ra[i] = ld16(a_ptr[i] + koff);
 #pragma unroll
         for (int i = 0; i < B_ITERS; ++i) {
-            // 16-row tiles (a few rows per expert) read every weight once:
-            // streamed past the caches, so they do not evict what is reused
-            // (decode 8-12% faster; the weight stream reaches 6.9 TB/s)
-            if constexpr (BM == 16)
+            // with about one row tile per expert every weight is read once:
+            // streamed past the caches, so it does not evict what is reused
+            // (decode 8-12% faster; the weight stream reaches 7.0 TB/s)
+            // (a compile-time choice: with a run-time branch the compiler
+            // merges the two loads into one plain load)
+            if constexpr (NTW)
                 rb[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(b_ptr[i] + koff * EB));
             else
                 rb[i] = ld16(b_ptr[i] + koff * EB);
@@ -363,17 +368,25 @@ __global__ __launch_bounds__(kThreads) void ffn_gemm_kernel(FfnArgs a) {
     }
 }
 
-template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP, bool FP8 = false, int SK = 64>
-hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP, bool FP8, int SK, bool NTW>
+hipError_t launch_gemm_nt(const FfnArgs& a, hipStream_t s) {
     constexpr int BN_OUT = GATEUP ? BN / 2 : BN;
     const int64_t mtiles = (a.P + BM - 1) / BM + (a.E < a.P ? a.E : a.P);
     const int64_t tiles = mtiles * (a.N / BN_OUT);
     const int64_t grid = (tiles + kNumXcd - 1) / kNumXcd * kNumXcd;
     if (grid <= 0) return hipSuccess;
     if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    ffn_gemm_kernel<BM, BN, WAVES_M, WAVES_N, GATEUP, FP8, SK>
+    ffn_gemm_kernel<BM, BN, WAVES_M, WAVES_N, GATEUP, FP8, SK, NTW>
         <<<dim3(static_cast<unsigned>(grid)), dim3(kThreads), 0, s>>>(a);
     return hipGetLastError();
+}
+
+// The small-tile GEMM with the weight loads streamed past the caches when
+// a.stream_w is set.
+template <int BM, int BN, int WAVES_M, int WAVES_N, bool GATEUP, bool FP8 = false, int SK = 64>
+hipError_t launch_gemm(const FfnArgs& a, hipStream_t s) {
+    if (a.stream_w) return launch_gemm_nt<BM, BN, WAVES_M, WAVES_N, GATEUP, FP8, SK, true>(a, s);
+    return launch_gemm_nt<BM, BN, WAVES_M, WAVES_N, GATEUP, FP8, SK, false>(a, s);
 }
 
 // The large tile reads its operands through buffer resources with 32-bit
@@ -831,6 +844,15 @@ hipError_t launch_gemm_dma(const FfnArgs& a, hipStream_t s) {
 // 64-row tiles, 3.9 ms with the large tile).  The 64-row tile remains for
 // shapes the large tile does not take.
 constexpr int64_t kSmallTileMaxRows = 12;
+// bf16 gate/up from there up to a mean of 32 rows per expert: 64-row tiles
+// with the weights streamed past the caches (512 tokens: 2.10 against 2.27 ms
+// on the large tile, 1024 tokens: 2.20 against 2.31 ms; at 1280 tokens they
+// draw level).  The down projection stays on the large tile there (the
+// 64-row tile was 2-6% slower for it).
+constexpr int64_t kBf16MidTileMaxRows = 32;
+// Weights stream past the caches when a 64-row tile covers an average
+// expert: each weight is then read about once.
+constexpr int64_t kStreamWeightsMaxRows = 64;
 // With FP8 weights the large tile streams more slowly at few rows (it widens
 // the codes inside its MFMA loop): 64-row tiles up to a mean of 48 rows
 // (1536 tokens: 2.29 ms for the expert FFN against 2.44 ms), the large tile
@@ -841,16 +863,18 @@ hipError_t launch_gate_up(const Problem& p, const uint16_t* x, const int32_t* so
                           const int32_t* offsets, const uint16_t* w_gate, const uint16_t* w_up,
                           uint16_t* h, hipStream_t s) {
     const int64_t P = p.T * p.k;
-    const FfnArgs a{P, p.T, p.k, p.E, p.H, p.I, x, sorted_pairs, offsets, w_gate, w_up, h,
-                    nullptr, nullptr};
+    FfnArgs a{P, p.T, p.k, p.E, p.H, p.I, x, sorted_pairs, offsets, w_gate, w_up, h,
+              nullptr, nullptr};
     const int64_t rows_per_expert = P / p.E;
+    a.stream_w = rows_per_expert <= kStreamWeightsMaxRows;
     // weight streaming in stages of K = 128 (H % 128 == 0 holds for every
     // accepted problem)
     if (rows_per_expert <= kSmallTileMaxRows)
         return launch_gemm<16, 128, 1, 4, true, false, 128>(a, s);
     // the large-tile kernel addresses x with 32-bit buffer offsets
     const bool x_fits = p.T * static_cast<int64_t>(p.H) * 2 <= static_cast<int64_t>(kNoRowOffset);
-    if (p.I % 128 != 0 || !x_fits) return launch_gemm<64, 128, 1, 4, true>(a, s);
+    if (rows_per_expert <= kBf16MidTileMaxRows || p.I % 128 != 0 || !x_fits)
+        return launch_gemm<64, 128, 1, 4, true>(a, s);
     return launch_gemm_dma<true>(a, s);
 }
 
@@ -861,6 +885,7 @@ hipError_t launch_down(const Problem& p, const uint16_t* h, const int32_t* offse
               nullptr};
     a.stream_out = P * static_cast<int64_t>(p.H) * 4 > kStreamBytes;
     const int64_t rows_per_expert = P / p.E;
+    a.stream_w = rows_per_expert <= kStreamWeightsMaxRows;
     if (rows_per_expert <= kSmallTileMaxRows) {
         // stages of K = 128 where I allows
         if (p.I % 128 == 0) return launch_gemm<16, 64, 1, 4, false, false, 128>(a, s);
@@ -886,8 +911,9 @@ hipError_t launch_expert_ffn_fp8(const Problem& p, const uint16_t* x, const int3
                                  float* y, hipStream_t s) {
     const int64_t P = p.T * p.k;
     const int64_t rows_per_expert = P / p.E;
-    const FfnArgs gu{P, p.T, p.k, p.E, p.H, p.I, x, sorted_pairs, offsets, w_gate, w_up, h,
-                     s_gate, s_up};
+    FfnArgs gu{P, p.T, p.k, p.E, p.H, p.I, x, sorted_pairs, offsets, w_gate, w_up, h,
+               s_gate, s_up};
+    gu.stream_w = rows_per_expert <= kStreamWeightsMaxRows;
     // few rows per expert: the weight stream is the cost; stages of K = 128
     // make every weight row of a stage one whole 128-byte line (gate/up: K = H,
     // and H % 128 == 0 holds for every accepted problem; down: where I allows)
@@ -903,6 +929,7 @@ hipError_t launch_expert_ffn_fp8(const Problem& p, const uint16_t* x, const int3
     FfnArgs dn{P, p.T, p.k, p.E, p.I, p.H, h, nullptr, offsets, w_down, nullptr, y, s_down,
                nullptr};
     dn.stream_out = P * static_cast<int64_t>(p.H) * 4 > kStreamBytes;
+    dn.stream_w = rows_per_expert <= kStreamWeightsMaxRows;
     if (rows_per_expert <= kSmallTileMaxRows && p.I % 128 == 0)
         return launch_gemm<16, 64, 1, 4, false, true, 128>(dn, s);
     if (rows_per_expert <= kFp8MidTileMaxRows || p.H % 256 != 0 || p.I % 128 != 0) {
