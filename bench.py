@@ -735,6 +735,13 @@ def kernels_only(args, weights):
             bb.copy_(a)
         torch.cuda.synchronize()
         del a, bb
+    if args.workload == "dense":  # the dense MLP's calls only
+        weights.clear()
+        torch.cuda.empty_cache()
+        print(json.dumps({"mode": "kernels-only", "workload": "dense-mlp", "steps": args.steps,
+                          "warmup": args.warmup, "dense_mlp": run_dense(args.steps, args.warmup)}),
+              flush=True)
+        return
     res = run_workload(args.workload, args.steps, args.warmup, weights, forward=False)
     line = {"mode": "kernels-only", "workload": f"beam-moe-{args.workload}", "steps": args.steps,
             "warmup": args.warmup,
@@ -765,7 +772,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "decode", "skew", "long"])
+                    choices=["prefill", "decode", "skew", "long", "dense"],
+                    help="the timed workload (dense: with --kernels-only only)")
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the secondary decode, skew and long measurements")
     ap.add_argument("--no-fp8", action="store_true",
@@ -827,6 +835,9 @@ def main():
     if args.kernels_only:
         kernels_only(args, weights)
         return
+    if args.workload == "dense":
+        raise SystemExit("--workload dense is a --kernels-only choice (the dense MLP is reported "
+                         "in the dense_mlp object of every bench line)")
 
     if args.copy_calibration:
         a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
