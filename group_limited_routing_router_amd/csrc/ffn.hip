@@ -15,9 +15,11 @@
 // rows are BN/2 gate rows and the BN/2 up rows of the same output columns, so
 // a lane holds gate and up accumulators of the same (row, col) and the SwiGLU
 // epilogue needs no data exchange.
-//   ffn_gemm_kernel      16- or 64-row tiles (few rows per expert: decode),
-//                        16x16x32 MFMA, K staged 64 or 128 at a time through
-//                        two padded LDS buffers via registers.
+//   ffn_gemm_kernel      16- or 64-row tiles (few rows per expert: decode
+//                        and small batches), 16x16x32 MFMA, K staged 64 or
+//                        128 at a time through two padded LDS buffers via
+//                        registers; with about one row tile per expert the
+//                        weights stream past the caches.
 //   ffn_gemm_dma_kernel  256 x 256 tiles (many rows per expert: prefill),
 //                        32x32x16 MFMA, operands loaded straight into LDS.
 //

@@ -128,3 +128,15 @@ def test_trace_and_counter_summaries(tmp_path, capsys):
     # 3000 KiB x 2 -> 6.144 MB read; 30 KiB x 1 -> 0.031 MB written
     assert abs(float(line[-2]) - 3000 * 2 * 1024 / 1e9) < 1e-3
     assert "x 2.000 x 1024" in out
+
+
+def test_kernel_source_sha_ignores_comments(tmp_path, monkeypatch):
+    src = tmp_path / "k.hip"
+    src.write_text("// a comment\\nint f() { return 1; } /* block */\\n")
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "KERNEL_SOURCES", ["k.hip"])
+    a = bench.kernel_source_sha()
+    src.write_text("// another comment\\nint f()  {\\n return 1; }\\n")
+    assert bench.kernel_source_sha() == a
+    src.write_text("int f() { return 2; }\\n")
+    assert bench.kernel_source_sha() != a

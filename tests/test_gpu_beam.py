@@ -49,7 +49,9 @@ def beam_weights():
 # large tile with mostly partly filled row tiles.
 # "huge": 212992 tokens, x above 2 GiB: the large tile's 32-bit buffer
 # offsets into x pass 2^31 (unsigned) for the later tokens
-EXTRA = {"mid": ("prefill", 1536), "huge": ("long", 212992)}
+# "t512": 512 tokens, 16 rows per expert: gate/up on 64-row tiles with the
+# weights streamed past the caches, down on the large tile
+EXTRA = {"mid": ("prefill", 1536), "t512": ("prefill", 512), "huge": ("long", 212992)}
 # first token whose x row starts at or past byte 2^31 (H = 5120, bf16)
 HUGE_FIRST_PAST = -(-(2 ** 31) // (5120 * 2))
 
@@ -63,7 +65,8 @@ def _cfg(name):
 
 @pytest.mark.parametrize("name,ffn_sample,seed",
                          [("decode", 128, 0), ("decode", 128, 1), ("decode", 128, 2),
-                          ("mid", 256, 0), ("prefill", 1024, 0), ("skew", 1024, 0),
+                          ("t512", 256, 0), ("mid", 256, 0), ("prefill", 1024, 0),
+                          ("skew", 1024, 0),
                           ("long", 2048, 0), ("huge", 64, 0)])
 def test_beam_config(moe, beam_weights, name, ffn_sample, seed):
     cfg = _cfg(name)

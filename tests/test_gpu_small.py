@@ -114,7 +114,8 @@ SHAPES = [
     (100, 256, 128, 4, 2, 1, 2),        # fewer experts than router waves
     (8230, 128, 64, 16, 4, 2, 4),       # above 8192 tokens: 64-token router tiles, ragged last tile
     (8300, 256, 64, 256, 8, 4, 8),      # the same with 256 experts
-    (600, 512, 256, 64, 8, 4, 4),       # ~38 rows per expert: large tiles of one or two row blocks (deep stream)
+    (600, 512, 256, 64, 8, 4, 4),       # ~38 rows per expert: large tiles of one or two row blocks
+    (400, 256, 128, 32, 4, 2, 2),       # ~25 rows per expert: 64-row gate/up tiles, weights streamed
 ]
 
 
