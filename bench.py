@@ -19,14 +19,16 @@ time of exactly --steps calls between two device synchronisations; the
 median and minimum per-step event times are reported beside it); `roofline`
 describes the dominant kernel (timed with HIP events on the stream the
 library launches on); `achievable_*` are this GPU's measured streaming-read
-bandwidth and back-to-back MFMA rate (the measurement kernels of
-include/moe_peak.h); `cpu_baseline` is the CPU oracle timed on this host's
+bandwidth and sustained back-to-back MFMA rate on pseudo-random operands
+(the measurement kernels of include/moe_peak.h); `cpu_baseline` is the CPU oracle timed on this host's
 cores (every decode token, samples of prefill and skew, long extrapolated).
 
 Other modes (one JSON line or a text table each):
   --kernels-only       only the timed workload's separate calls (the kernel
                        trace of such a run holds nothing else)
   --gemm-study         the prefill expert GEMMs at fixed rows per expert
+  --power-study        board power and graphics clock (amd-smi samples) while
+                       each kernel runs back to back
   --summarize-trace D  per-kernel durations from a rocprofv3 kernel trace
   --summarize-pmc D1 D2  HBM bytes per launch from FETCH_SIZE / WRITE_SIZE runs
   --summarize-counters D per-kernel averages of any counter run
@@ -42,6 +44,7 @@ import os
 import re
 import statistics
 import sys
+import time
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
@@ -300,7 +303,11 @@ def achievable_peaks(repeats=5):
     (include/moe_peak.h): a streaming read of 8 GiB (far larger than the
     256 MB Infinity Cache) over several grid sizes, with and without the
     nontemporal cache policy, and back-to-back bf16 MFMAs on register operands
-    over several grid sizes.  The best rate of each is reported."""
+    over two grid sizes, on pseudo-random operands (the rate reported as
+    achievable) and on one fixed operand pattern.  The reads are the best of
+    `repeats` calls; the MFMA loops run for about a second each and report the
+    mean of the second half, since the board power limit takes effect only
+    after the first tens of milliseconds."""
     import torch
 
     from group_limited_routing_router_amd import moe
@@ -322,6 +329,17 @@ def achievable_peaks(repeats=5):
             times.append(e0.elapsed_time(e1))
         return min(times)
 
+    def sustained_ms(fn, n):
+        for _ in range(n):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
     reads = {}
     for nt in (False, True):
         for wg in (2048, 8192, 16384, 32768):
@@ -331,23 +349,30 @@ def achievable_peaks(repeats=5):
     torch.cuda.empty_cache()
     mfma = {}
     iters = 20000
-    for wg in (1024, 2048):
-        out = torch.empty(4 * wg, dtype=torch.float32, device="cuda")
-        flops = moe.moe_peak_mfma_bf16(iters, out, wg)  # also the warm-up call
-        ms = best_ms(lambda: moe.moe_peak_mfma_bf16(iters, out, wg))
-        mfma[f"wg{wg}"] = round(flops / (ms * 1e-3) / 1e12, 1)
-        del out
+    for rnd in (True, False):
+        for wg in (1024, 2048):
+            out = torch.empty(4 * wg, dtype=torch.float32, device="cuda")
+            flops = moe.moe_peak_mfma_bf16(iters, out, wg, random_operands=rnd)
+            ms = sustained_ms(lambda: moe.moe_peak_mfma_bf16(iters, out, wg, random_operands=rnd),
+                              max(4, int(round(500 / (flops / 2.0e15 * 1e3)))))
+            mfma[f"{'random' if rnd else 'fixed'}_wg{wg}"] = round(flops / (ms * 1e-3) / 1e12, 1)
+            del out
     hbm = max(reads.values())
-    tf = max(mfma.values())
+    tf = max(v for k, v in mfma.items() if k.startswith("random"))
+    tf_fixed = max(v for k, v in mfma.items() if k.startswith("fixed"))
     log("[bench] achievable: read %s GB/s, bf16 MFMA %s TFLOP/s" % (reads, mfma))
     return {"achievable_hbm_gbs": hbm, "achievable_hbm_frac_of_peak": round(hbm * 1e9 / PEAK_HBM, 4),
             "achievable_mfma_tflops": tf,
             "achievable_mfma_frac_of_peak": round(tf * 1e12 / PEAK_BF16, 4),
+            "mfma_fixed_operands_tflops": tf_fixed,
             "read_gbs_by_grid": reads, "mfma_tflops_by_grid": mfma,
             "how": "moe_peak_stream_read: one read of 8 GiB, 16-byte loads, 8 in flight per lane, "
-                   "256-thread workgroups; moe_peak_mfma_bf16: 8 independent 32x32x16 bf16 "
-                   f"MFMA chains per wave, {iters} steps, 4 waves per workgroup; best of "
-                   f"{repeats} event-timed calls per grid"}
+                   f"256-thread workgroups, best of {repeats} event-timed calls per grid; "
+                   "moe_peak_mfma_bf16: 8 independent 32x32x16 bf16 MFMA chains per wave on "
+                   f"register operands, {iters} steps, 4 waves per workgroup, the mean of about "
+                   "0.5 s of calls after 0.5 s of the same calls; achievable_mfma_tflops is the "
+                   "rate on pseudo-random operands (bits change at every issue, as on real "
+                   "data), mfma_fixed_operands_tflops the rate on one fixed pattern"}
 
 
 def gemm_study(weights, steps, warmup):
@@ -426,6 +451,173 @@ def gemm_study(weights, steps, warmup):
     print(json.dumps({"study": "prefill expert GEMMs by rows per expert",
                       "workload": "beam-moe-prefill", "steps": steps, "warmup": warmup,
                       "rows_per_expert": rows, "library_bmm_256_rows": lib}), flush=True)
+
+
+class _PowerSampler:
+    """Samples the board's socket power, graphics clocks and temperatures with
+    `amd-smi metric` (read-only) in a background thread, about four times a
+    second, each sample stamped with the wall time."""
+
+    def __init__(self):
+        import shutil
+        import threading
+        self.samples, self.error = [], None
+        self.exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def parse(text):
+        pw = re.search(r"SOCKET_POWER:\s*(\d+)", text)
+        clk = [int(v) for v in re.findall(r"GFX_\d+:\s*\n\s*CLK:\s*(\d+)", text)]
+        hot = re.search(r"HOTSPOT:\s*(\d+)", text)
+        return dict(power_w=int(pw.group(1)) if pw else None,
+                    gfx_mhz=sum(clk) / len(clk) if clk else None,
+                    hotspot_c=int(hot.group(1)) if hot else None)
+
+    def _run(self):
+        import subprocess
+        while not self._stop.is_set():
+            t = time.time()
+            try:
+                r = subprocess.run([self.exe, "metric", "-g", "0", "-p", "-c", "-t"],
+                                   capture_output=True, text=True, timeout=10)
+                smp = self.parse(r.stdout)
+                if smp["power_w"] is None and smp["gfx_mhz"] is None:
+                    self.error = (r.stdout + r.stderr).strip()[-300:]
+                else:
+                    self.samples.append(((t + time.time()) / 2, smp))
+            except (OSError, subprocess.SubprocessError) as e:
+                self.error = repr(e)
+                return
+            self._stop.wait(0.25)
+
+    def __enter__(self):
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        self._thread.join(timeout=15)
+
+    def window(self, t0, t1):
+        """Mean and extremes over the samples in [t0, t1]."""
+        ss = [s for t, s in self.samples if t0 <= t <= t1]
+
+        def col(key):
+            return [s[key] for s in ss if s[key] is not None]
+        pw, ck, hot = col("power_w"), col("gfx_mhz"), col("hotspot_c")
+        return dict(samples=len(ss),
+                    power_w=round(sum(pw) / len(pw)) if pw else None,
+                    power_w_max=max(pw) if pw else None,
+                    gfx_mhz=round(sum(ck) / len(ck)) if ck else None,
+                    gfx_mhz_min=round(min(ck)) if ck else None,
+                    hotspot_c_max=max(hot) if hot else None)
+
+
+def power_study(weights, seconds):
+    """Board power, graphics clock and rate of the block's kernels and of the
+    measurement kernels, each run back to back for `seconds` while
+    `amd-smi metric` samples the board (the first half second of a phase is
+    left out of its averages).  Prints one line per phase and one JSON line."""
+    import torch
+
+    from group_limited_routing_router_amd import moe
+    from group_limited_routing_router_amd.inputs import CONFIGS, make_tokens
+
+    def setup(name):
+        cfg = CONFIGS[name]
+        d = make_tokens(cfg, seed=0, device="cuda")
+        d.update(weights)
+        p = moe.MoEProblem.from_config(cfg)
+        b = moe.alloc_buffers(p)
+        moe.moe_route(p, d["x"], d["w_router"], d["bias"], b["topk_ids"], b["topk_weights"])
+        moe.moe_permute(p, b["topk_ids"], b["expert_offsets"], b["sorted_pairs"], b["pair_rows"],
+                        b["ws"])
+        n_hit = int((torch.bincount(b["topk_ids"].flatten().long(), minlength=cfg.E) > 0).sum())
+        counts, layer = work_counts(cfg, n_hit)
+        torch.cuda.synchronize()
+        return cfg, p, d, b, counts, layer
+
+    phases = []
+
+    def phase(label, fn, flops=None, nbytes=None, what=""):
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.time()
+        e0.record()
+        n = 0
+        if fn is None:
+            time.sleep(seconds)
+        else:
+            while time.time() - t0 < seconds:
+                for _ in range(5):
+                    fn()
+                n += 5
+                torch.cuda.synchronize()
+        e1.record()
+        torch.cuda.synchronize()
+        t1 = time.time()
+        ent = dict(phase=label, what=what, calls=n)
+        if n:
+            ms = e0.elapsed_time(e1) / n
+            ent["ms_per_call"] = round(ms, 4)
+            if flops:
+                ent["tflops"] = round(flops / (ms * 1e-3) / 1e12, 1)
+                ent["frac_bf16_peak"] = round(flops / (ms * 1e-3) / PEAK_BF16, 4)
+            if nbytes:
+                ent["gbs"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+        ent.update(sampler.window(t0 + 0.5, t1))
+        phases.append(ent)
+        log("[power] %-22s %s" % (label, {k: v for k, v in ent.items() if k not in ("phase", "what")}))
+
+    with _PowerSampler() as sampler:
+        phase("idle", None, what="no kernel")
+        iters, wg = 20000, 2048
+        sink = torch.empty(4 * wg, dtype=torch.float32, device="cuda")
+        fl = moe.moe_peak_mfma_bf16(iters, sink, wg, random_operands=False)
+        phase("mfma_fixed_operands", lambda: moe.moe_peak_mfma_bf16(iters, sink, wg, False),
+              flops=fl, what="moe_peak_mfma_bf16, one fixed operand pattern")
+        phase("mfma_random_operands", lambda: moe.moe_peak_mfma_bf16(iters, sink, wg, True),
+              flops=fl, what="moe_peak_mfma_bf16, pseudo-random operands")
+        buf = torch.empty(8 << 30, dtype=torch.uint8, device="cuda")
+        buf.fill_(0x5A)
+        s2 = torch.zeros(4, dtype=torch.int32, device="cuda")
+        phase("stream_read_nt", lambda: moe.moe_peak_stream_read(buf, s2, 32768, nontemporal=True),
+              nbytes=buf.numel(), what="moe_peak_stream_read, 8 GiB, nontemporal, 32768 workgroups")
+        del buf, s2, sink
+        torch.cuda.empty_cache()
+        for name in ("decode", "prefill", "long"):
+            cfg, p, d, b, counts, layer = setup(name)
+
+            def gate_up():
+                moe.moe_expert_gate_up(p, d["x"], b["sorted_pairs"], b["expert_offsets"],
+                                       d["w_gate"], d["w_up"], b["h"])
+
+            def down():
+                moe.moe_expert_down(p, b["h"], b["expert_offsets"], d["w_down"], b["y"])
+
+            def forward():
+                moe.moe_forward(p, d["x"], d["w_router"], d["bias"], d["w_gate"], d["w_up"],
+                                d["w_down"], b["out"], b["topk_ids"], b["topk_weights"], b["y"],
+                                b["ws"])
+            tag = f"{cfg.name} T={cfg.T}"
+            phase(f"{cfg.name}_gate_up", gate_up, flops=counts["gate_up"]["flops"],
+                  nbytes=counts["gate_up"]["bytes"], what=f"moe_expert_gate_up, {tag}")
+            if name == "prefill":
+                phase(f"{cfg.name}_down", down, flops=counts["down"]["flops"],
+                      nbytes=counts["down"]["bytes"], what=f"moe_expert_down, {tag}")
+            if name != "long":
+                phase(f"{cfg.name}_forward", forward, flops=layer["flops"], nbytes=layer["bytes"],
+                      what=f"moe_forward, {tag}")
+            del b, d
+            torch.cuda.empty_cache()
+        phase("idle_after", None, what="no kernel")
+    if sampler.error and not sampler.samples:
+        log("[power] amd-smi gave no samples: %s" % sampler.error)
+    print(json.dumps({"study": "board power and graphics clock by kernel",
+                      "seconds_per_phase": seconds, "sampler": "amd-smi metric -g 0 -p -c -t",
+                      "phases": phases}), flush=True)
 
 
 def roofline_for(res, kernel):
@@ -794,6 +986,11 @@ def main():
     ap.add_argument("--gemm-study", action="store_true",
                     help="instead of the benchmark: the prefill expert GEMMs at fixed rows per "
                          "expert next to the library batched GEMM (one JSON line)")
+    ap.add_argument("--power-study", action="store_true",
+                    help="instead of the benchmark: board power and clock while each kernel runs "
+                         "back to back (amd-smi samples; one JSON line)")
+    ap.add_argument("--seconds", type=float, default=3.0,
+                    help="with --power-study: seconds per phase")
     ap.add_argument("--kernels-only", action="store_true",
                     help="instead of the benchmark: the workload's steps as separate calls only")
     ap.add_argument("--with-fp8", action="store_true",
@@ -836,6 +1033,9 @@ def main():
     torch.cuda.synchronize()
     if args.gemm_study:
         gemm_study(weights, args.steps, args.warmup)
+        return
+    if args.power_study:
+        power_study(weights, args.seconds)
         return
     if args.kernels_only:
         kernels_only(args, weights)

@@ -52,18 +52,57 @@ __global__ __launch_bounds__(kPeakThreads) void stream_read_kernel(const u32x4* 
 // matrix pipe always has an independent MFMA to issue.
 constexpr int kChains = 8;
 
-__global__ __launch_bounds__(kPeakThreads) void mfma_loop_kernel(int64_t iters,
+// splitmix64 finalizer (Steele, Lea and Flood, "Fast splittable pseudorandom
+// number generators", 2014): a bijective mix of a 64-bit counter.
+__device__ __forceinline__ uint64_t mix64(uint64_t z) {
+    z += 0x9e3779b97f4a7c15ull;
+    z = (z ^ (z >> 30)) * 0xbf58476d1ce4e5b9ull;
+    z = (z ^ (z >> 27)) * 0x94d049bb133111ebull;
+    return z ^ (z >> 31);
+}
+
+// Two bf16 values from 32 random bits: random sign and 7-bit mantissa,
+// exponent 2^-5 .. 2^-2, so magnitudes lie in [2^-5, 2^-1).
+__device__ __forceinline__ uint32_t random_bf16_pair(uint32_t r) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t q = r >> (16 * h);
+        const uint32_t bits = ((q & 1u) << 15) | ((122u + ((q >> 1) & 3u)) << 7) | ((q >> 3) & 0x7fu);
+        w |= bits << (16 * h);
+    }
+    return w;
+}
+
+__global__ __launch_bounds__(kPeakThreads) void mfma_loop_kernel(int64_t iters, int random_operands,
                                                                  float* __restrict__ sink) {
     const int lane = threadIdx.x & 63;
-    u32x4 ra, rb;
+    const uint64_t tid = static_cast<uint64_t>(blockIdx.x) * kPeakThreads + threadIdx.x;
+    bf16x8 a[kChains], b[kChains];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        // bf16 operands: a = 1 + lane / 128, b about 2^-9, so the sums stay
-        // far from overflow over any number of steps that fits the run
-        ra[i] = 0x3f803f80u + static_cast<uint32_t>(lane);
-        rb[i] = 0x3b003b00u + static_cast<uint32_t>(i);
+    for (int c = 0; c < kChains; ++c) {
+        u32x4 ra, rb;
+#pragma unroll
+        for (int i = 0; i < 4; i += 2) {
+            if (random_operands) {
+                // chain c takes its own operands, different on every lane
+                const uint64_t za = mix64((tid * kChains + c) * 4 + i / 2);
+                const uint64_t zb = mix64((tid * kChains + c) * 4 + 2 + i / 2);
+                ra[i] = random_bf16_pair(static_cast<uint32_t>(za));
+                ra[i + 1] = random_bf16_pair(static_cast<uint32_t>(za >> 32));
+                rb[i] = random_bf16_pair(static_cast<uint32_t>(zb));
+                rb[i + 1] = random_bf16_pair(static_cast<uint32_t>(zb >> 32));
+            } else {
+                // fixed bf16 operands: a = 1 + lane / 128, b about 2^-9, so
+                // the sums stay far from overflow over any number of steps
+                ra[i] = ra[i + 1] = 0x3f803f80u + static_cast<uint32_t>(lane);
+                rb[i] = 0x3b003b00u + static_cast<uint32_t>(i);
+                rb[i + 1] = 0x3b003b00u + static_cast<uint32_t>(i + 1);
+            }
+        }
+        a[c] = as_bf16x8(ra);
+        b[c] = as_bf16x8(rb);
     }
-    const bf16x8 a = as_bf16x8(ra), b = as_bf16x8(rb);
     f32x16 acc[kChains];
 #pragma unroll
     for (int c = 0; c < kChains; ++c)
@@ -71,7 +110,7 @@ __global__ __launch_bounds__(kPeakThreads) void mfma_loop_kernel(int64_t iters,
         for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
     for (int64_t it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int c = 0; c < kChains; ++c) acc[c] = mfma32(a, b, acc[c]);
+        for (int c = 0; c < kChains; ++c) acc[c] = mfma32(a[c], b[c], acc[c]);
     }
     float s = 0.0f;
 #pragma unroll
@@ -102,10 +141,11 @@ MOE_EXPORT moe_status moe_peak_stream_read(const void* buf, size_t bytes, int no
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
-MOE_EXPORT moe_status moe_peak_mfma_bf16(int64_t iters, float* sink, int workgroups,
-                                         hipStream_t stream) {
+MOE_EXPORT moe_status moe_peak_mfma_bf16(int64_t iters, int random_operands, float* sink,
+                                         int workgroups, hipStream_t stream) {
     if (!sink || iters < 1 || workgroups < 1) return MOE_ERR_INVALID_ARG;
-    moe::mfma_loop_kernel<<<dim3(workgroups), dim3(moe::kPeakThreads), 0, stream>>>(iters, sink);
+    moe::mfma_loop_kernel<<<dim3(workgroups), dim3(moe::kPeakThreads), 0, stream>>>(
+        iters, random_operands != 0, sink);
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 

@@ -122,7 +122,7 @@ def load_library():
         lib.moe_forward_noalloc.restype = st
         lib.moe_peak_stream_read.argtypes = [P, ctypes.c_size_t, ctypes.c_int, P, ctypes.c_int, P]
         lib.moe_peak_stream_read.restype = st
-        lib.moe_peak_mfma_bf16.argtypes = [ctypes.c_int64, P, ctypes.c_int, P]
+        lib.moe_peak_mfma_bf16.argtypes = [ctypes.c_int64, ctypes.c_int, P, ctypes.c_int, P]
         lib.moe_peak_mfma_bf16.restype = st
         lib.moe_peak_mfma_bf16_flops.argtypes = [ctypes.c_int64, ctypes.c_int]
         lib.moe_peak_mfma_bf16_flops.restype = ctypes.c_double
@@ -261,11 +261,13 @@ def moe_peak_stream_read(buf, sink, workgroups, nontemporal=False, stream=None):
                                                 int(workgroups), _stream(stream)))
 
 
-def moe_peak_mfma_bf16(iters, sink, workgroups, stream=None):
-    """The back-to-back bf16 MFMA loop; `sink` holds 4 * workgroups floats.
-    Returns the FLOPs of the call."""
+def moe_peak_mfma_bf16(iters, sink, workgroups, random_operands=True, stream=None):
+    """The back-to-back bf16 MFMA loop on pseudo-random (default) or fixed
+    register operands; `sink` holds 4 * workgroups floats.  Returns the FLOPs
+    of the call."""
     lib = load_library()
-    _check(lib.moe_peak_mfma_bf16(int(iters), _p(sink), int(workgroups), _stream(stream)))
+    _check(lib.moe_peak_mfma_bf16(int(iters), int(bool(random_operands)), _p(sink),
+                                  int(workgroups), _stream(stream)))
     return float(lib.moe_peak_mfma_bf16_flops(int(iters), int(workgroups)))
 
 

@@ -38,8 +38,19 @@ moe_status moe_peak_stream_read(const void* buf, size_t bytes, int nontemporal, 
  * steps of 8 independent 32x32x16 bf16 MFMAs on register operands (no memory
  * traffic), then writes one float: sink[wave index], sink holding
  * 4 * workgroups floats.  moe_peak_mfma_bf16_flops gives the FLOPs of one
- * call (2 * 32 * 32 * 16 per MFMA). */
-moe_status moe_peak_mfma_bf16(int64_t iters, float* sink, int workgroups, hipStream_t stream);
+ * call (2 * 32 * 32 * 16 per MFMA).
+ *   random_operands  0: one fixed operand pattern for every chain and step
+ *                    (few bits change from one MFMA to the next);
+ *                    nonzero: each chain of each lane holds its own
+ *                    pseudo-random bf16 operands (random sign and mantissa,
+ *                    magnitudes 2^-5 .. 2^-1, from the splitmix64 mix of the
+ *                    thread and chain index), so the bits change at every
+ *                    issue as they do in a GEMM on real data.  The matrix
+ *                    pipes draw more power on changing bits; where the board
+ *                    power limit binds, the random rate is the lower one and
+ *                    is the ceiling a GEMM on such data can meet. */
+moe_status moe_peak_mfma_bf16(int64_t iters, int random_operands, float* sink, int workgroups,
+                              hipStream_t stream);
 
 double moe_peak_mfma_bf16_flops(int64_t iters, int workgroups);
 

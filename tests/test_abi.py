@@ -193,8 +193,9 @@ def test_measurement_kernels_reject_bad_arguments(lib):
     assert cdll.moe_peak_stream_read(good, 4008, 0, good, 16, None) == 1   # not a multiple of 16
     assert cdll.moe_peak_stream_read(odd, 4096, 0, good, 16, None) == 1    # misaligned
     assert cdll.moe_peak_stream_read(good, 4096, 0, good, 0, None) == 1    # no workgroups
-    assert cdll.moe_peak_mfma_bf16(i64(0), good, 16, None) == 1
-    assert cdll.moe_peak_mfma_bf16(i64(10), None, 16, None) == 1
+    assert cdll.moe_peak_mfma_bf16(i64(0), 1, good, 16, None) == 1
+    assert cdll.moe_peak_mfma_bf16(i64(10), 0, None, 16, None) == 1
+    assert cdll.moe_peak_mfma_bf16(i64(10), 1, good, 0, None) == 1      # no workgroups
     # FLOPs of one call: waves x steps x 8 chains x 2*32*32*16
     assert lib.load_library().moe_peak_mfma_bf16_flops(i64(100), 3) == 3 * 4 * 100 * 8 * 32768
 

@@ -140,3 +140,21 @@ def test_kernel_source_sha_ignores_comments(tmp_path, monkeypatch):
     assert bench.kernel_source_sha() == a
     src.write_text("int f() { return 2; }\\n")
     assert bench.kernel_source_sha() != a
+
+
+def test_power_sampler_parse_and_window():
+    text = ("GPU: 0\n    POWER:\n        SOCKET_POWER: 1396 W\n        GFX_VOLTAGE: N/A\n"
+            "    CLOCK:\n        GFX_0:\n            CLK: 1600 MHz\n            MIN_CLK: 231 MHz\n"
+            "        GFX_1:\n            CLK: 1620 MHz\n            MAX_CLK: 2400 MHz\n"
+            "    TEMPERATURE:\n        EDGE: N/A\n        HOTSPOT: 55 °C\n        MEM: 40 °C\n")
+    smp = bench._PowerSampler.parse(text)
+    assert smp == {"power_w": 1396, "gfx_mhz": 1610.0, "hotspot_c": 55}
+    assert bench._PowerSampler.parse("amd-smi: no devices") == {
+        "power_w": None, "gfx_mhz": None, "hotspot_c": None}
+    s = bench._PowerSampler()
+    s.samples = [(1.0, smp), (2.0, dict(smp, power_w=1400, gfx_mhz=1590.0)),
+                 (5.0, dict(smp, power_w=300))]
+    w = s.window(0.5, 2.5)
+    assert w["samples"] == 2 and w["power_w"] == 1398 and w["power_w_max"] == 1400
+    assert w["gfx_mhz"] == 1600 and w["gfx_mhz_min"] == 1590 and w["hotspot_c_max"] == 55
+    assert s.window(10, 11)["power_w"] is None
