@@ -232,6 +232,8 @@ def workload_summary(res, peaks=None):
         out["hot_expert_share"] = res["hot_share"]
     out["kernels_ms"] = {k: round(v, 4) for k, v in kms.items() if k != "combine_residual"}
     out["roofline"] = roofline_for(res, dominant)
+    if peaks:
+        at_intensity(out["roofline"], peaks)
     return out
 
 
@@ -345,7 +347,21 @@ def achievable_peaks(repeats=5):
         for wg in (2048, 8192, 16384, 32768):
             ms = best_ms(lambda: moe.moe_peak_stream_read(buf, sink, wg, nontemporal=nt))
             reads[f"{'nt' if nt else 'cached'}_wg{wg}"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
-    del buf, sink
+    # LDS-fed MFMAs with an HBM stream of 0, 1, 2 and 4 16-byte loads a lane
+    # per 16 MFMAs (one workgroup per compute unit, four rounds); each call
+    # reads at most the 8 GiB buffer once
+    mixed = []
+    wg_mix = 1024
+    fsink = torch.empty(4 * wg_mix, dtype=torch.float32, device="cuda")
+    for nl in (0, 1, 2, 4):
+        steps = 1000 if nl == 0 else (nbytes // (wg_mix * 256 * 16) // nl - 8) // 8 * 8
+        flops, nb = moe.moe_peak_mfma_stream(buf, nl, steps, fsink, wg_mix)
+        ms = sustained_ms(lambda: moe.moe_peak_mfma_stream(buf, nl, steps, fsink, wg_mix),
+                          max(4, int(round(500 / (flops / 1.5e15 * 1e3)))))
+        mixed.append({"loads_per_step": nl, "bytes_per_kflop": round(nb / flops * 1e3, 3),
+                      "tflops": round(flops / (ms * 1e-3) / 1e12, 1),
+                      "gbs": round(nb / (ms * 1e-3) / 1e9, 1)})
+    del buf, sink, fsink
     torch.cuda.empty_cache()
     mfma = {}
     iters = 20000
@@ -360,19 +376,24 @@ def achievable_peaks(repeats=5):
     hbm = max(reads.values())
     tf = max(v for k, v in mfma.items() if k.startswith("random"))
     tf_fixed = max(v for k, v in mfma.items() if k.startswith("fixed"))
-    log("[bench] achievable: read %s GB/s, bf16 MFMA %s TFLOP/s" % (reads, mfma))
+    log("[bench] achievable: read %s GB/s, bf16 MFMA %s TFLOP/s, with a stream %s" % (
+        reads, mfma, mixed))
     return {"achievable_hbm_gbs": hbm, "achievable_hbm_frac_of_peak": round(hbm * 1e9 / PEAK_HBM, 4),
             "achievable_mfma_tflops": tf,
             "achievable_mfma_frac_of_peak": round(tf * 1e12 / PEAK_BF16, 4),
             "mfma_fixed_operands_tflops": tf_fixed,
             "read_gbs_by_grid": reads, "mfma_tflops_by_grid": mfma,
+            "mfma_with_hbm_stream": mixed,
             "how": "moe_peak_stream_read: one read of 8 GiB, 16-byte loads, 8 in flight per lane, "
                    f"256-thread workgroups, best of {repeats} event-timed calls per grid; "
                    "moe_peak_mfma_bf16: 8 independent 32x32x16 bf16 MFMA chains per wave on "
                    f"register operands, {iters} steps, 4 waves per workgroup, the mean of about "
                    "0.5 s of calls after 0.5 s of the same calls; achievable_mfma_tflops is the "
                    "rate on pseudo-random operands (bits change at every issue, as on real "
-                   "data), mfma_fixed_operands_tflops the rate on one fixed pattern"}
+                   "data), mfma_fixed_operands_tflops the rate on one fixed pattern; "
+                   "moe_peak_mfma_stream: per step and wave 8 LDS fragment reads of random "
+                   "bf16 and their 16 MFMAs, with 0-4 nontemporal 16-byte loads a lane of an "
+                   "8 GiB buffer, 1024 workgroups, timed like the MFMA loop"}
 
 
 def gemm_study(weights, steps, warmup):
@@ -585,7 +606,15 @@ def power_study(weights, seconds):
         s2 = torch.zeros(4, dtype=torch.int32, device="cuda")
         phase("stream_read_nt", lambda: moe.moe_peak_stream_read(buf, s2, 32768, nontemporal=True),
               nbytes=buf.numel(), what="moe_peak_stream_read, 8 GiB, nontemporal, 32768 workgroups")
-        del buf, s2, sink
+        fsink = torch.empty(4 * 1024, dtype=torch.float32, device="cuda")
+        for nl in (0, 1, 2, 4):
+            steps = 1000 if nl == 0 else (buf.numel() // (1024 * 256 * 16) // nl - 8) // 8 * 8
+            fl2, nb2 = moe.moe_peak_mfma_stream(buf, nl, steps, fsink, 1024)
+            phase(f"mfma_lds_stream_{nl}", lambda: moe.moe_peak_mfma_stream(buf, nl, steps, fsink, 1024),
+                  flops=fl2, nbytes=nb2 or None,
+                  what=f"moe_peak_mfma_stream, {nl} loads a lane per 16 MFMAs "
+                       f"({nb2 / fl2 * 1e3:.2f} bytes per kFLOP)")
+        del buf, s2, sink, fsink
         torch.cuda.empty_cache()
         for name in ("decode", "prefill", "long"):
             cfg, p, d, b, counts, layer = setup(name)
@@ -618,6 +647,25 @@ def power_study(weights, seconds):
     print(json.dumps({"study": "board power and graphics clock by kernel",
                       "seconds_per_phase": seconds, "sampler": "amd-smi metric -g 0 -p -c -t",
                       "phases": phases}), flush=True)
+
+
+def at_intensity(roof, peaks):
+    """Add to a roofline object the rate moe_peak_mfma_stream reaches at the
+    largest measured intensity not above the kernel's algorithmic bytes per
+    thousand FLOPs (a ceiling at least as high as the one at the kernel's own
+    intensity), and the kernel's fraction of it."""
+    if not roof.get("algorithmic_flops"):
+        return
+    ai = roof["algorithmic_bytes"] / roof["algorithmic_flops"] * 1e3
+    pts = [m for m in peaks.get("mfma_with_hbm_stream", []) if m["bytes_per_kflop"] <= ai]
+    if not pts or ai > max(m["bytes_per_kflop"] for m in peaks["mfma_with_hbm_stream"]):
+        return
+    best = max(pts, key=lambda m: m["bytes_per_kflop"])
+    tflops = roof["algorithmic_flops"] / (roof["ms"] * 1e-3) / 1e12
+    roof["bytes_per_kflop"] = round(ai, 3)
+    roof["achievable_mfma_tflops_at_intensity"] = best["tflops"]
+    roof["achievable_at_bytes_per_kflop"] = best["bytes_per_kflop"]
+    roof["mfma_frac_of_achievable_at_intensity"] = round(tflops / best["tflops"], 4)
 
 
 def roofline_for(res, kernel):
@@ -1090,6 +1138,7 @@ def main():
     }
     out["graph_replay"] = graph_replay_ms(main_res, args.steps, args.warmup)
     if peaks:
+        at_intensity(out["roofline"], peaks)
         out["achievable_hbm_gbs"] = peaks["achievable_hbm_gbs"]
         out["achievable_mfma_tflops"] = peaks["achievable_mfma_tflops"]
         out["achievable"] = peaks

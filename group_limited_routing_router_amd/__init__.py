@@ -10,6 +10,7 @@ _BINDING_NAMES = (
     "moe_route", "moe_permute", "moe_expert_ffn", "moe_expert_gate_up", "moe_expert_down",
     "moe_combine", "moe_combine_residual", "moe_dense_mlp", "moe_expert_ffn_fp8", "moe_forward",
     "moe_forward_fp8", "moe_forward_noalloc", "moe_peak_stream_read", "moe_peak_mfma_bf16",
+    "moe_peak_mfma_stream",
     "moe_workspace_bytes", "MoEProblem", "MoEError", "DTYPE_F32", "DTYPE_BF16",
     "load_library", "library_path",
 )

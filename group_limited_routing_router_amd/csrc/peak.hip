@@ -121,6 +121,93 @@ __global__ __launch_bounds__(kPeakThreads) void mfma_loop_kernel(int64_t iters, 
         sink[static_cast<int64_t>(blockIdx.x) * (kPeakThreads / kWave) + (threadIdx.x >> 6)] = s;
 }
 
+// MFMAs fed from LDS with an HBM stream beside them, in the proportions of a
+// GEMM: per step every wave reads four A and four B fragments (16 bytes a
+// lane each) from a 16 KB LDS region of its own holding pseudo-random bf16
+// values (a window that moves every step, so no read repeats the last one)
+// and issues the 16 MFMAs of their 4 x 4 outer product (the per-wave ratio
+// of a 128 x 128 wave tile), and every lane issues NL nontemporal
+// 16-byte loads from the buffer, consumed kStreamAhead steps later so the
+// loads are in flight under the MFMAs.  Thread t reads chunks
+// t + (s * NL + j) * nthreads for steps s = 0 .. steps + kStreamAhead - 1, so
+// the launch reads one contiguous span of the buffer once.  The XOR of the
+// loaded data decides whether a value is added to the sum each wave stores,
+// which keeps the loads alive.
+constexpr int kStreamAhead = 8;
+constexpr int kMixLdsChunks = 4096;  // 64 KB: 1024 16-byte chunks per wave
+
+template <int NL>
+__global__ __launch_bounds__(kPeakThreads) void mfma_stream_kernel(const u32x4* __restrict__ src,
+                                                                   int64_t steps,
+                                                                   float* __restrict__ sink) {
+    __shared__ u32x4 s_frag[kMixLdsChunks];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t nthreads = static_cast<int64_t>(gridDim.x) * kPeakThreads;
+    const int64_t tid = static_cast<int64_t>(blockIdx.x) * kPeakThreads + threadIdx.x;
+    for (int i = threadIdx.x; i < kMixLdsChunks; i += kPeakThreads) {
+        const uint64_t z = mix64(static_cast<uint64_t>(blockIdx.x) * kMixLdsChunks + i);
+        u32x4 v;
+        v[0] = random_bf16_pair(static_cast<uint32_t>(z));
+        v[1] = random_bf16_pair(static_cast<uint32_t>(z >> 32));
+        const uint64_t z2 = mix64(z);
+        v[2] = random_bf16_pair(static_cast<uint32_t>(z2));
+        v[3] = random_bf16_pair(static_cast<uint32_t>(z2 >> 32));
+        s_frag[i] = v;
+    }
+    __syncthreads();
+    f32x16 acc[16];
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[c][i] = 0.0f;
+    const u32x4* p = src + tid;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    u32x4 ring[kStreamAhead][NL > 0 ? NL : 1];
+#pragma unroll
+    for (int d = 0; d < kStreamAhead; ++d)
+#pragma unroll
+        for (int j = 0; j < NL; ++j)
+            ring[d][j] = __builtin_nontemporal_load(p + static_cast<int64_t>(d * NL + j) * nthreads);
+    const int base = wave * (kMixLdsChunks / 4) + lane;
+    for (int64_t s0 = 0; s0 < steps; s0 += kStreamAhead) {
+#pragma unroll
+        for (int d = 0; d < kStreamAhead; ++d) {
+            const int64_t st = s0 + d;
+#pragma unroll
+            for (int j = 0; j < NL; ++j) {
+                x ^= ring[d][j];
+                ring[d][j] = __builtin_nontemporal_load(p + ((st + kStreamAhead) * NL + j) * nthreads);
+            }
+            // the read window moves by 72 chunks a step (wrapping within the
+            // wave's region; not a divisor of the unrolled 8 steps' span), so
+            // the reads stay in the loop
+            const int off = base + static_cast<int>((st * 72) & 511);
+            u32x4 fa[4], fb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                fa[j] = s_frag[off + j * 64];
+                fb[j] = s_frag[off + 256 + j * 64];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i * 4 + j] = mfma32(as_bf16x8(fa[i]), as_bf16x8(fb[j]), acc[i * 4 + j]);
+        }
+    }
+#pragma unroll
+    for (int d = 0; d < kStreamAhead; ++d)
+#pragma unroll
+        for (int j = 0; j < NL; ++j) x ^= ring[d][j];
+    float sum = ((x[0] ^ x[1] ^ x[2] ^ x[3]) == 0x9e3779b9u) ? 1.0f : 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sum += acc[c][i];
+    if (lane == 0) sink[static_cast<int64_t>(blockIdx.x) * (kPeakThreads / kWave) + wave] = sum;
+}
+
 }  // namespace
 }  // namespace moe
 
@@ -153,4 +240,41 @@ MOE_EXPORT double moe_peak_mfma_bf16_flops(int64_t iters, int workgroups) {
     // waves x steps x chains x (2 * 32 * 32 * 16) FLOP
     return static_cast<double>(workgroups) * (moe::kPeakThreads / moe::kWave) *
            static_cast<double>(iters) * moe::kChains * 2.0 * 32 * 32 * 16;
+}
+
+MOE_EXPORT moe_status moe_peak_mfma_stream(const void* buf, size_t bytes, int loads_per_step,
+                                           int64_t steps, float* sink, int workgroups,
+                                           hipStream_t stream) {
+    if (!sink || workgroups < 1 || steps < moe::kStreamAhead || steps % moe::kStreamAhead != 0)
+        return MOE_ERR_INVALID_ARG;
+    if (loads_per_step != 0 && loads_per_step != 1 && loads_per_step != 2 && loads_per_step != 4)
+        return MOE_ERR_INVALID_ARG;
+    if (loads_per_step > 0) {
+        // every chunk the launch reads lies inside the buffer
+        const double need = static_cast<double>(steps + moe::kStreamAhead) * loads_per_step *
+                            workgroups * moe::kPeakThreads * 16.0;
+        if (!buf || reinterpret_cast<uintptr_t>(buf) % 16 != 0 || static_cast<double>(bytes) < need)
+            return MOE_ERR_INVALID_ARG;
+    }
+    const auto* src = static_cast<const moe::u32x4*>(buf);
+    const dim3 grid(workgroups), block(moe::kPeakThreads);
+    switch (loads_per_step) {
+        case 0: moe::mfma_stream_kernel<0><<<grid, block, 0, stream>>>(src, steps, sink); break;
+        case 1: moe::mfma_stream_kernel<1><<<grid, block, 0, stream>>>(src, steps, sink); break;
+        case 2: moe::mfma_stream_kernel<2><<<grid, block, 0, stream>>>(src, steps, sink); break;
+        default: moe::mfma_stream_kernel<4><<<grid, block, 0, stream>>>(src, steps, sink); break;
+    }
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE_EXPORT double moe_peak_mfma_stream_flops(int64_t steps, int workgroups) {
+    // waves x steps x 16 MFMAs x (2 * 32 * 32 * 16) FLOP
+    return static_cast<double>(workgroups) * (moe::kPeakThreads / moe::kWave) *
+           static_cast<double>(steps) * 16 * 2.0 * 32 * 32 * 16;
+}
+
+MOE_EXPORT double moe_peak_mfma_stream_bytes(int64_t steps, int loads_per_step, int workgroups) {
+    // bytes consumed by the steps (the last kStreamAhead steps' loads come on top)
+    return static_cast<double>(workgroups) * moe::kPeakThreads * static_cast<double>(steps) *
+           loads_per_step * 16.0;
 }

@@ -54,7 +54,8 @@ EXPORTS = ("moe_workspace_bytes", "moe_route", "moe_permute", "moe_expert_ffn",
            "moe_dense_mlp", "moe_expert_ffn_fp8", "moe_forward", "moe_forward_fp8",
            "moe_forward_noalloc", "moe_status_string", "moe_last_error",
            # measurement kernels (include/moe_peak.h)
-           "moe_peak_stream_read", "moe_peak_mfma_bf16", "moe_peak_mfma_bf16_flops")
+           "moe_peak_stream_read", "moe_peak_mfma_bf16", "moe_peak_mfma_bf16_flops",
+           "moe_peak_mfma_stream", "moe_peak_mfma_stream_flops", "moe_peak_mfma_stream_bytes")
 
 
 def library_path() -> str:
@@ -126,6 +127,13 @@ def load_library():
         lib.moe_peak_mfma_bf16.restype = st
         lib.moe_peak_mfma_bf16_flops.argtypes = [ctypes.c_int64, ctypes.c_int]
         lib.moe_peak_mfma_bf16_flops.restype = ctypes.c_double
+        lib.moe_peak_mfma_stream.argtypes = [P, ctypes.c_size_t, ctypes.c_int, ctypes.c_int64, P,
+                                             ctypes.c_int, P]
+        lib.moe_peak_mfma_stream.restype = st
+        lib.moe_peak_mfma_stream_flops.argtypes = [ctypes.c_int64, ctypes.c_int]
+        lib.moe_peak_mfma_stream_flops.restype = ctypes.c_double
+        lib.moe_peak_mfma_stream_bytes.argtypes = [ctypes.c_int64, ctypes.c_int, ctypes.c_int]
+        lib.moe_peak_mfma_stream_bytes.restype = ctypes.c_double
         lib.moe_status_string.argtypes = [ctypes.c_int]
         lib.moe_status_string.restype = ctypes.c_char_p
         lib.moe_last_error.argtypes = []
@@ -269,6 +277,19 @@ def moe_peak_mfma_bf16(iters, sink, workgroups, random_operands=True, stream=Non
     _check(lib.moe_peak_mfma_bf16(int(iters), int(bool(random_operands)), _p(sink),
                                   int(workgroups), _stream(stream)))
     return float(lib.moe_peak_mfma_bf16_flops(int(iters), int(workgroups)))
+
+
+def moe_peak_mfma_stream(buf, loads_per_step, steps, sink, workgroups, stream=None):
+    """LDS-fed bf16 MFMAs with `loads_per_step` 16-byte HBM loads a lane per
+    step from `buf` (a GPU tensor, or None with 0 loads); `sink` holds
+    4 * workgroups floats.  Returns (FLOPs, bytes) of the call."""
+    lib = load_library()
+    nbytes = 0 if buf is None else buf.numel() * buf.element_size()
+    _check(lib.moe_peak_mfma_stream(_p(buf) if buf is not None else None, nbytes,
+                                    int(loads_per_step), int(steps), _p(sink), int(workgroups),
+                                    _stream(stream)))
+    return (float(lib.moe_peak_mfma_stream_flops(int(steps), int(workgroups))),
+            float(lib.moe_peak_mfma_stream_bytes(int(steps), int(loads_per_step), int(workgroups))))
 
 
 def alloc_buffers(p: MoEProblem, device="cuda", out_dtype=torch.float32):

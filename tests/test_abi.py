@@ -196,6 +196,19 @@ def test_measurement_kernels_reject_bad_arguments(lib):
     assert cdll.moe_peak_mfma_bf16(i64(0), 1, good, 16, None) == 1
     assert cdll.moe_peak_mfma_bf16(i64(10), 0, None, 16, None) == 1
     assert cdll.moe_peak_mfma_bf16(i64(10), 1, good, 0, None) == 1      # no workgroups
+    # the MFMA loop with an HBM stream: steps a multiple of 8, loads 0/1/2/4,
+    # and a buffer holding every chunk the launch reads
+    sz = ctypes.c_size_t
+    need = (64 + 8) * 2 * 16 * 256 * 16
+    assert cdll.moe_peak_mfma_stream(good, sz(need), 2, i64(60), good, 16, None) == 1  # not x8
+    assert cdll.moe_peak_mfma_stream(good, sz(need), 3, i64(64), good, 16, None) == 1  # loads
+    assert cdll.moe_peak_mfma_stream(good, sz(need - 16), 2, i64(64), good, 16, None) == 1
+    assert cdll.moe_peak_mfma_stream(odd, sz(need), 2, i64(64), good, 16, None) == 1
+    assert cdll.moe_peak_mfma_stream(None, sz(need), 2, i64(64), good, 16, None) == 1
+    assert cdll.moe_peak_mfma_stream(good, sz(need), 2, i64(64), None, 16, None) == 1
+    assert cdll.moe_peak_mfma_stream(good, sz(need), 2, i64(64), good, 0, None) == 1
+    assert lib.load_library().moe_peak_mfma_stream_flops(i64(64), 3) == 3 * 4 * 64 * 16 * 32768
+    assert lib.load_library().moe_peak_mfma_stream_bytes(i64(64), 2, 3) == 3 * 256 * 64 * 2 * 16
     # FLOPs of one call: waves x steps x 8 chains x 2*32*32*16
     assert lib.load_library().moe_peak_mfma_bf16_flops(i64(100), 3) == 3 * 4 * 100 * 8 * 32768
 

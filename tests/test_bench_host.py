@@ -158,3 +158,21 @@ def test_power_sampler_parse_and_window():
     assert w["samples"] == 2 and w["power_w"] == 1398 and w["power_w_max"] == 1400
     assert w["gfx_mhz"] == 1600 and w["gfx_mhz_min"] == 1590 and w["hotspot_c_max"] == 55
     assert s.window(10, 11)["power_w"] is None
+
+
+def test_ceiling_at_intensity_picks_the_point_below():
+    peaks = {"mfma_with_hbm_stream": [
+        {"loads_per_step": 0, "bytes_per_kflop": 0.0, "tflops": 1800.0},
+        {"loads_per_step": 1, "bytes_per_kflop": 1.953, "tflops": 1500.0},
+        {"loads_per_step": 2, "bytes_per_kflop": 3.906, "tflops": 1300.0},
+        {"loads_per_step": 4, "bytes_per_kflop": 7.812, "tflops": 750.0}]}
+    # 4.03 bytes per kFLOP (prefill gate/up): the 3.906 point, 1300 TFLOP/s
+    roof = {"algorithmic_bytes": 4.03e9, "algorithmic_flops": 1e12, "ms": 1.0}
+    bench.at_intensity(roof, peaks)
+    assert roof["achievable_at_bytes_per_kflop"] == 3.906
+    assert roof["achievable_mfma_tflops_at_intensity"] == 1300.0
+    assert abs(roof["mfma_frac_of_achievable_at_intensity"] - 1000.0 / 1300.0) < 1e-4
+    # an HBM-bound kernel past the largest measured intensity gets nothing
+    roof = {"algorithmic_bytes": 250e9, "algorithmic_flops": 1e12, "ms": 1.0}
+    bench.at_intensity(roof, peaks)
+    assert "achievable_mfma_tflops_at_intensity" not in roof
