@@ -1,8 +1,8 @@
-// peak.hip -- two measurement kernels that anchor the roofline: the streaming
-// read bandwidth and the bf16 MFMA rate this GPU sustains (declared in
-// include/moe_peak.h).  They compute nothing of the MoE block; the benchmark
-// reports the block's kernels against these figures next to the published
-// peaks.
+// peak.hip -- measurement kernels that anchor the roofline (declared in
+// include/moe_peak.h): the streaming read bandwidth, the bf16 MFMA rate, and
+// the MFMA rate beside an HBM stream in a GEMM's proportions that this GPU
+// sustains.  They compute nothing of the MoE block; the benchmark reports the
+// block's kernels against these figures next to the published peaks.
 #include "common.h"
 #include "moe_peak.h"
 
@@ -16,8 +16,8 @@ constexpr int kReadUnroll = 8;  // independent 16-byte loads in flight per lane
 
 // Every lane reads kReadUnroll 16-byte chunks per step, the chunks of one step
 // one grid width (all threads) apart, and the workgroups walk the buffer
-// together (grid stride), so each step of the grid covers one contiguous span.  The XOR of everything
-// read is stored only if it equals a value it practically never takes, which
+// together (grid stride), so each step of the grid covers one contiguous
+// span.  The XOR of everything read is stored only if it equals a value it practically never takes, which
 // keeps the loads alive without a write stream.
 template <bool NT>
 __global__ __launch_bounds__(kPeakThreads) void stream_read_kernel(const u32x4* __restrict__ src,
@@ -48,8 +48,9 @@ __global__ __launch_bounds__(kPeakThreads) void stream_read_kernel(const u32x4* 
 
 // Each wave runs `iters` steps of kChains independent 32x32x16 bf16 MFMAs on
 // operands held in registers (no memory traffic inside the loop), then stores
-// one sum per wave so the chains stay live.  With four waves per SIMD the
-// matrix pipe always has an independent MFMA to issue.
+// one sum per wave so the chains stay live.  The eight chains keep the matrix
+// pipe issuing back to back: no MFMA waits for the result of the one before
+// it.
 constexpr int kChains = 8;
 
 // splitmix64 finalizer (Steele, Lea and Flood, "Fast splittable pseudorandom
