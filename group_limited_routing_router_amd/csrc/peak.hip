@@ -17,8 +17,9 @@ constexpr int kReadUnroll = 8;  // independent 16-byte loads in flight per lane
 // Every lane reads kReadUnroll 16-byte chunks per step, the chunks of one step
 // one grid width (all threads) apart, and the workgroups walk the buffer
 // together (grid stride), so each step of the grid covers one contiguous
-// span.  The XOR of everything read is stored only if it equals a value it practically never takes, which
-// keeps the loads alive without a write stream.
+// span.  The XOR of everything read is stored only if it equals a value it
+// practically never takes, which keeps the loads alive without a write
+// stream.
 template <bool NT>
 __global__ __launch_bounds__(kPeakThreads) void stream_read_kernel(const u32x4* __restrict__ src,
                                                                    int64_t chunks, uint32_t key,
