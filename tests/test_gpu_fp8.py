@@ -60,6 +60,8 @@ SMALL = [
     (300, 256, 192, 8, 2, 1, 2),      # ~75 rows per expert, I not a multiple of 128: 64-row tiles
     (160, 256, 256, 8, 2, 1, 2),      # ~40 rows per expert: 64-row tiles, both reductions in stages of 128
     (300, 256, 256, 8, 2, 1, 2),      # ~75 rows per expert: large tiles
+    (300, 65536, 128, 8, 2, 1, 2),    # the largest H: large tiles over K = 65536
+    (24, 128, 65536, 8, 2, 1, 2),     # the largest I: 16-row tiles, down over K = 65536
 ]
 
 

@@ -116,6 +116,13 @@ SHAPES = [
     (8300, 256, 64, 256, 8, 4, 8),      # the same with 256 experts
     (600, 512, 256, 64, 8, 4, 4),       # ~38 rows per expert: large tiles of one or two row blocks
     (400, 256, 128, 32, 4, 2, 2),       # ~25 rows per expert: 64-row gate/up tiles, weights streamed
+    # the largest H and I the library takes (65536), on the large tile (75
+    # rows per expert; gate/up over K = 65536, or K = 128 in two stages) and
+    # on 16-row tiles (6 rows per expert)
+    (300, 65536, 128, 8, 2, 1, 2),
+    (300, 128, 65536, 8, 2, 1, 2),
+    (24, 65536, 128, 8, 2, 1, 2),
+    (24, 128, 65536, 8, 2, 1, 2),
 ]
 
 
