@@ -20,8 +20,10 @@ median and minimum per-step event times are reported beside it); `roofline`
 describes the dominant kernel (timed with HIP events on the stream the
 library launches on); `achievable_*` are this GPU's measured streaming-read
 bandwidth and sustained back-to-back MFMA rate on pseudo-random operands
-(the measurement kernels of include/moe_peak.h); `cpu_baseline` is the CPU oracle timed on this host's
-cores (every decode token, samples of prefill and skew, long extrapolated).
+(the measurement kernels of include/moe_peak.h), and `roofline` adds the
+MFMA rate those kernels reach beside an HBM stream of the kernel's own bytes
+per FLOP; `cpu_baseline` is the CPU oracle timed on this host's cores (every
+decode token, samples of prefill and skew, long extrapolated).
 
 Other modes (one JSON line or a text table each):
   --kernels-only       only the timed workload's separate calls (the kernel
