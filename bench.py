@@ -299,7 +299,8 @@ def run_dense(steps, warmup):
             "roofline": {"bound": "mfma", "achieved": round(flops / (ms * 1e-3) / 1e12, 1),
                          "peak": PEAK_BF16 / 1e12, "unit": "TFLOP/s",
                          "frac": round(flops / (ms * 1e-3) / PEAK_BF16, 4), "traffic": None,
-                         "algorithmic_bytes": bytes_, "algorithmic_flops": flops}}
+                         "ms": round(ms, 4), "algorithmic_bytes": bytes_,
+                         "algorithmic_flops": flops}}
 
 
 def achievable_peaks(repeats=5):
@@ -1170,6 +1171,8 @@ def main():
         torch.cuda.empty_cache()
     if not args.no_dense:
         out["dense_mlp"] = run_dense(args.steps, args.warmup)
+        if peaks:
+            at_intensity(out["dense_mlp"]["roofline"], peaks)
         log("[bench] dense MLP T=%d I=%d: %.3f ms/step, %.1f%% of bf16 MFMA peak" % (
             out["dense_mlp"]["tokens"], out["dense_mlp"]["intermediate"],
             out["dense_mlp"]["ms_per_step"], 100 * out["dense_mlp"]["roofline"]["frac"]))
